@@ -1,0 +1,140 @@
+"""CPU oracle for the FP32 GEMM C = op(A) . op(B).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+package.  The HIP library neither imports nor links anything here, and this
+package imports nothing from the HIP library.
+
+``gemm_ref`` returns the plain definition of the product (a k-ordered double
+precision sum per output element, see ``gemm_ref.c``) as a float64 array.
+``schedule`` emulates the memory-access schedules the pages count, to pin
+the operation and traffic figures the benchmark divides by.
+
+Parity status of each function is recorded in its docstring; every function
+here is pinned by ``tests/test_oracle_pins.py`` or ``tests/test_counts.py``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+_lock = threading.Lock()
+_libs = {}
+
+_i64 = ctypes.c_int64
+_ptr = ctypes.c_void_p
+
+
+def load(path: Optional[str] = None) -> "Oracle":
+    """Load (building first if absent) the oracle library at ``path``."""
+    path = path or _build.LIBRARY
+    with _lock:
+        if path not in _libs:
+            if not os.path.exists(path):
+                if path != _build.LIBRARY:
+                    raise FileNotFoundError(path)
+                _build.build()
+            _libs[path] = Oracle(path)
+        return _libs[path]
+
+
+def _as_stored(x: np.ndarray) -> np.ndarray:
+    if x.dtype != np.float32 or x.ndim != 2:
+        raise TypeError("operands are 2-D float32 arrays of shape (rows, ld)")
+    return np.ascontiguousarray(x)
+
+
+class Oracle:
+    """ctypes view of one built oracle library."""
+
+    def __init__(self, path: str):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.gemm_ref_f64.restype = ctypes.c_int
+        lib.gemm_ref_f64.argtypes = [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64,
+                                     _ptr, _i64, ctypes.c_int, ctypes.c_int, _ptr]
+        lib.gemm_ref_f64_entries.restype = ctypes.c_int
+        lib.gemm_ref_f64_entries.argtypes = [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64,
+                                             ctypes.c_int, ctypes.c_int, _i64,
+                                             _ptr, _ptr, _ptr]
+        lib.gemm_ref_threads.restype = ctypes.c_int
+        lib.gemm_ref_threads.argtypes = []
+        self._lib = lib
+
+    def threads(self) -> int:
+        return int(self._lib.gemm_ref_threads())
+
+    def gemm(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+             transA: int = 0, transB: int = 0,
+             with_stats: bool = False):
+        """C = op(A) . op(B) in float64, shape (M, N).
+
+        ``A`` and ``B`` are stored matrices of shape (rows, ld) as produced by
+        ``gemm_inputs`` (the leading dimension is the array's second extent).
+        With ``with_stats`` also returns (multiply-adds, operand reads).
+        Pinned: identity, all-ones, rank-1, brute force against exact
+        rationals, numpy float64 matmul.
+        """
+        A = _as_stored(A)
+        B = _as_stored(B)
+        C = np.zeros((M, max(N, 1)), dtype=np.float64)
+        stats = np.zeros(2, dtype=np.int64)
+        rc = self._lib.gemm_ref_f64(M, N, K, A.ctypes.data, A.shape[1],
+                                    B.ctypes.data, B.shape[1], C.ctypes.data,
+                                    C.shape[1], int(transA), int(transB),
+                                    stats.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (status {rc})")
+        C = C[:, :N]
+        if with_stats:
+            return C, (int(stats[0]), int(stats[1]))
+        return C
+
+    def entries(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+                transA: int, transB: int, rows: np.ndarray,
+                cols: np.ndarray) -> np.ndarray:
+        """C[rows[t], cols[t]] for each t, in float64.  Same definition as ``gemm``.
+
+        Pinned against ``gemm`` entry by entry and by the same closed forms.
+        """
+        A = _as_stored(A)
+        B = _as_stored(B)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        if rows.shape != cols.shape:
+            raise ValueError("rows and cols differ in length")
+        out = np.empty(rows.shape, dtype=np.float64)
+        rc = self._lib.gemm_ref_f64_entries(M, N, K, A.ctypes.data, A.shape[1],
+                                            B.ctypes.data, B.shape[1], int(transA),
+                                            int(transB), rows.size, rows.ctypes.data,
+                                            cols.ctypes.data, out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (status {rc})")
+        return out
+
+
+def gemm_ref(A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+             transA: int = 0, transB: int = 0) -> np.ndarray:
+    """Module-level shorthand for ``load().gemm(...)``."""
+    return load().gemm(A, B, M, N, K, transA, transB)
+
+
+def gemm_ref_entries(A, B, M, N, K, transA, transB, rows, cols) -> np.ndarray:
+    """Module-level shorthand for ``load().entries(...)``."""
+    return load().entries(A, B, M, N, K, transA, transB, rows, cols)
+
+
+def tolerance(C_ref: np.ndarray, K: int) -> Tuple[np.ndarray, float]:
+    """The acceptance bounds for an FP32 result against the float64 oracle.
+
+    Elementwise: |C_gpu - C_ref| <= 1e-6*K + 1e-5*|C_ref|.
+    Whole matrix: ||C_gpu - C_ref||_F / ||C_ref||_F <= 1e-6.
+    """
+    return 1e-6 * K + 1e-5 * np.abs(C_ref), 1e-6

@@ -1,0 +1,25 @@
+"""Shared pytest configuration.
+
+Markers: ``gpu`` tests need an MI355X (gfx950) and the built HIP library;
+everything else runs on the CPU.
+"""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+@pytest.fixture(scope="session")
+def oracle():
+    import oracle as oracle_pkg
+    return oracle_pkg.load()
