@@ -1,14 +1,300 @@
-"""Benchmark placeholder: model functions only (the runner follows)."""
+"""Throughput of the FP32 GEMM library on one MI355X.
 
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload S4k] [--algo auto]
+
+One step is one C = A.B of the workload (default: the 4096^3 square
+product the throughput metric is quoted on), with A, B and C resident in
+HBM before timing starts.  W untimed steps, then exactly K steps between
+two device synchronisations, timed with HIP events recorded on the stream
+the library launches on (PyTorch's current stream).  Prints ONE JSON line.
+
+Besides the metric the line carries:
+  roofline      the GEMM kernel against the MI355X FP32 matrix peak
+                (157.3 TFLOP/s), with HBM traffic from rocprofv3 counters
+                when the committed counter summary matches these sources;
+  cpu_baseline  the CPU oracle timed on a bounded row-panel of the same
+                product on this host's cores (a reported baseline, not a target);
+  context       the other kernel families (vector FMA, LDS-tiled, naive with
+                its 1/4 flop-per-byte HBM model) and torch.mm on the same
+                inputs, for comparison;
+  parity        a sampled check of the timed result against the oracle.
+
+``--copy-probe`` instead runs a plain device copy of known size, the
+scale reference for the HBM byte counters.  ``--gpus`` above 1 exits:
+this benchmark measures one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+MI355X_FP32_PEAK_TFLOPS = 157.3   # 256 CU x 2.4 GHz x 256 FLOP/clk/CU (matrix and packed vector)
+MI355X_HBM_TBPS = 8.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# -------------------------------------------------- algorithmic work models ---
 
 def gemm_flops(M: int, N: int, K: int) -> int:
+    """2*M*N*K: a multiply and an add per (i, j, k) term."""
     return 2 * M * N * K
 
 
 def naive_model_bytes(M: int, N: int, K: int) -> int:
+    """The naive kernel's traffic model: every term reads one float of A and
+    one of B from HBM (8 bytes per multiply-add), caches ignored."""
     return 8 * M * N * K
 
 
 def tiled_model_bytes(M: int, N: int, K: int, BM: int, BN: int) -> int:
+    """Global->shared traffic of a BM x BN-tiled product: each of the
+    ceil(M/BM)*ceil(N/BN) tiles reads a BM x K panel of A and a K x BN panel of B."""
     tiles = -(-M // BM) * -(-N // BN)
     return 4 * K * tiles * (BM + BN)
+
+
+def compulsory_bytes(M: int, N: int, K: int) -> int:
+    """Read A and B once, write C once."""
+    return 4 * (M * K + K * N + M * N)
+
+
+def source_digest() -> str:
+    """Hash of the HIP sources; counter summaries are valid only for this digest."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "dense_fp32_matrix_gemm_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """Per-launch HBM bytes from profiles/traffic_<kernel>_<workload>.md, or None
+    if absent or taken from different sources."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_digest") != source_digest():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ runner ---
+
+def _timed(fn, steps: int, warmup: int):
+    """Average ms per call of fn over `steps` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def _lscpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, target_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on a row panel of the workload's product."""
+    import numpy as np
+    import oracle
+    orc = oracle.load()
+    A, B = w.make_a(), w.make_b()
+
+    def run(rows: int) -> float:
+        # a panel of `rows` rows of C: the same product restricted to A's first rows
+        a_panel = A[:, :rows] if w.transA else A[:rows]
+        t0 = time.perf_counter()
+        orc.gemm(np.ascontiguousarray(a_panel), B, rows, w.N, w.K, w.transA, w.transB)
+        return time.perf_counter() - t0
+
+    probe_rows = max(1, min(w.M, 16))
+    t_probe = run(probe_rows)
+    rows = int(min(w.M, max(probe_rows, target_s / max(t_probe, 1e-9) * probe_rows)))
+    t = run(rows)
+    tflops = gemm_flops(rows, w.N, w.K) / t / 1e12
+    return {"value": tflops, "unit": "TFLOPS", "cores": orc.threads(), "kind": "oracle",
+            "sample": f"first {rows} of {w.M} rows of C ({w.name}: {w.M}x{w.N}x{w.K}), "
+                      f"{t:.1f} s, FP64-accumulating triple loop, OpenMP over rows",
+            "host_cpu": _lscpu_model(), "os_cpu_count": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def copy_probe(mib: int = 1024, reps: int = 5) -> None:
+    """A plain device copy of `mib` MiB, the scale reference for FETCH/WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "bytes_written": n * 4, "reps": reps}))
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "fma", "tiled", "naive"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: the GEMM has no multi-GPU path in this library.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import gemm_inputs as gi
+    import dense_fp32_matrix_gemm_amd as g
+
+    if args.copy_probe:
+        copy_probe()
+        return 0
+
+    torch.backends.cuda.matmul.allow_tf32 = False
+    name = args.workload or gi.HEADLINE
+    w = gi.WORKLOADS[name]
+    lib_path = g.library_path()
+    g.load()  # fail loudly now if the HIP library is missing
+
+    A, B, C = w.make_a(), w.make_b(), w.make_c()
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.from_numpy(C).cuda()
+    stream = torch.cuda.current_stream()
+    algo_id = g.ALGOS[args.algo]
+
+    def step(algo=algo_id):
+        st = g.gemm_f32_ex(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
+                           dC.data_ptr(), w.ldc_, w.transA, w.transB, stream.cuda_stream, algo)
+        if st != 0:
+            raise g.GemmError(st)
+
+    flops = gemm_flops(w.M, w.N, w.K)
+    torch.cuda.synchronize()
+    ms = _timed(step, args.steps, args.warmup)
+    value = flops / (ms * 1e-3) / 1e12
+
+    # sampled parity of the timed result (expected values from the oracle only)
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows, cols = gi.sample_entries(w.M, w.N, 256, seed=23)
+        ref = oracle.load().entries(A, B, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
+        got = dC.cpu().numpy()[rows, cols].astype(np.float64)
+        ratio = np.abs(got - ref) / (1e-6 * w.K + 1e-5 * np.abs(ref))
+        parity = {"entries": int(rows.size), "max_err_over_bound": float(np.max(ratio)),
+                  "ok": bool(np.all(ratio <= 1.0))}
+
+    kernel = "gemm_f32_" + ("mfma" if args.algo == "auto" else args.algo)
+    roofline = {"bound": "mfma", "achieved": value, "peak": MI355X_FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": value / MI355X_FP32_PEAK_TFLOPS,
+                "traffic": read_traffic(kernel, name),
+                "kernel": kernel, "flops_per_launch": flops,
+                "compulsory_bytes": compulsory_bytes(w.M, w.N, w.K)}
+    if args.algo == "naive":
+        model = naive_model_bytes(w.M, w.N, w.K) / (ms * 1e-3) / 1e9
+        roofline.update(bound="hbm", achieved=model, peak=MI355X_HBM_TBPS * 1000,
+                        unit="GB/s", frac=model / (MI355X_HBM_TBPS * 1000))
+    elif args.algo == "fma":
+        roofline["peak_note"] = "vector FP32 without packed FMA peaks at 78.6 TFLOP/s"
+
+    context = None
+    if not args.no_context:
+        context = {}
+        for other in ("mfma", "fma", "tiled", "naive"):
+            if other == args.algo or (other == "mfma" and args.algo == "auto"):
+                continue
+            reps = 3 if other == "naive" else 10
+            oms = _timed(lambda: step(g.ALGOS[other]), reps, 1)
+            entry = {"tflops": flops / (oms * 1e-3) / 1e12, "ms": oms}
+            if other == "naive":
+                gbps = naive_model_bytes(w.M, w.N, w.K) / (oms * 1e-3) / 1e9
+                roof = MI355X_HBM_TBPS * 1e12 / 4 / 1e12
+                entry.update(model_gbps=gbps, model_roofline_tflops=roof,
+                             frac_of_model_roofline=entry["tflops"] / roof)
+            context[other] = entry
+        # the vendor library through PyTorch, same shapes (a labelled comparison)
+        ta = dA[:, :w.a_dims[1]]
+        tb = dB[:, :w.b_dims[1]]
+        ta = ta.t() if w.transA else ta
+        tb = tb.t() if w.transB else tb
+        out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        tms = _timed(lambda: torch.mm(ta, tb, out=out), 10, 2)
+        context["torch.mm"] = {"tflops": flops / (tms * 1e-3) / 1e12, "ms": tms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w)
+
+    line = {
+        "metric": "FP32 GEMM TFLOPS (2MNK/s) and % of MI355X FP32 peak at N=4096",
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda_,
+                   "ldb": w.ldb_, "ldc": w.ldc_, "transA": w.transA, "transB": w.transB,
+                   "inputs": w.description, "seeds": [w.seed_a, w.seed_b],
+                   "algo": args.algo, "parallelism": "single GPU"},
+        "pct_of_peak": 100.0 * value / MI355X_FP32_PEAK_TFLOPS,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "context": context,
+        "parity": parity,
+        "library": os.path.relpath(lib_path, ROOT),
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

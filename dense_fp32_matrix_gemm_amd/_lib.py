@@ -1,0 +1,84 @@
+"""ctypes binding of ``libgemm_f32.so`` (declarations: include/gemm_f32.h).
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  Loading fails loudly if the library has not been built; there
+is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from . import build as _build
+
+ALGO_AUTO, ALGO_MFMA, ALGO_FMA, ALGO_TILED, ALGO_NAIVE = 0, 1, 2, 3, 4
+ALGOS = {"auto": ALGO_AUTO, "mfma": ALGO_MFMA, "fma": ALGO_FMA, "tiled": ALGO_TILED,
+         "naive": ALGO_NAIVE}
+
+# Every symbol include/gemm_f32.h declares, with (restype, argtypes).
+_i64, _ptr, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+_GEMM_ARGS = [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr]
+SIGNATURES = {
+    "gemm_f32": (_int, _GEMM_ARGS),
+    "gemm_f32_naive": (_int, _GEMM_ARGS),
+    "gemm_f32_ex": (_int, _GEMM_ARGS + [_int]),
+    "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
+    "gemm_f32_version": (_int, []),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.environ.get("GEMM_F32_LIBRARY", _build.LIBRARY)
+
+
+def load() -> ctypes.CDLL:
+    """The loaded library (loaded once per process)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise LibraryNotBuilt(
+                    f"{path} is missing: build it with `python -m dense_fp32_matrix_gemm_amd.build` "
+                    "(or __graft_entry__.build()); there is no non-HIP fallback")
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+        return _lib
+
+
+def _call(name, *args) -> int:
+    return int(getattr(load(), name)(*args))
+
+
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream) -> int:
+    """C = op(A) . op(B); pointers are device addresses (ints), stream a hipStream_t (int or None)."""
+    return _call("gemm_f32", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream)
+
+
+def gemm_f32_naive(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream) -> int:
+    return _call("gemm_f32_naive", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream)
+
+
+def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream, algo) -> int:
+    return _call("gemm_f32_ex", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream, algo)
+
+
+def gemm_f32_strerror(status: int) -> str:
+    return load().gemm_f32_strerror(int(status)).decode()
+
+
+def gemm_f32_version() -> int:
+    return _call("gemm_f32_version")

@@ -1,0 +1,121 @@
+// gemm_api.hip -- the C ABI of the FP32 GEMM library: argument validation,
+// kernel selection and launch-error mapping.  Contract: include/gemm_f32.h.
+//
+// Validation happens entirely on the host, before any HIP call, so invalid
+// arguments are reported with the same codes on a machine without a GPU.
+#include "gemm_f32.h"
+#include "gemm_internal.hpp"
+
+#include <climits>
+
+namespace {
+
+using gemmf32::Problem;
+
+constexpr int64_t kDimLimit = int64_t(INT_MAX);  // dimensions are < 2^31
+
+// Argument positions (1-based) as in the prototypes, for the -i codes.
+enum Arg {
+    kArgM = 1, kArgN, kArgK, kArgA, kArgLda, kArgB, kArgLdb, kArgC, kArgLdc,
+    kArgTransA, kArgTransB, kArgStream, kArgAlgo
+};
+
+int validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+             const float *B, int64_t ldb, const float *C, int64_t ldc,
+             int transA, int transB)
+{
+    if (M < 0 || M > kDimLimit) return -kArgM;
+    if (N < 0 || N > kDimLimit) return -kArgN;
+    if (K < 0 || K > kDimLimit) return -kArgK;
+    if (transA != 0 && transA != 1) return -kArgTransA;
+    if (transB != 0 && transB != 1) return -kArgTransB;
+    const int64_t a_row = transA ? M : K;   // length of a stored row of A
+    const int64_t b_row = transB ? K : N;   // length of a stored row of B
+    if (A == nullptr && M * K > 0) return -kArgA;
+    if (lda < (a_row > 1 ? a_row : 1) || lda > kDimLimit) return -kArgLda;
+    if (B == nullptr && K * N > 0) return -kArgB;
+    if (ldb < (b_row > 1 ? b_row : 1) || ldb > kDimLimit) return -kArgLdb;
+    if (C == nullptr && M * N > 0) return -kArgC;
+    if (ldc < (N > 1 ? N : 1) || ldc > kDimLimit) return -kArgLdc;
+    return 0;
+}
+
+int run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+        const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
+        int transB, void *stream, int algo)
+{
+    const int bad = validate(M, N, K, A, lda, B, ldb, C, ldc, transA, transB);
+    if (bad) return bad;
+    if (algo < GEMM_F32_ALGO_AUTO || algo > GEMM_F32_ALGO_NAIVE) return -kArgAlgo;
+    if (M == 0 || N == 0) return 0;  // nothing to write
+
+    const Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (K == 0) {
+        err = gemmf32::launch_zero_fill(p, s);
+    } else {
+        switch (algo) {
+        case GEMM_F32_ALGO_NAIVE: err = gemmf32::launch_naive(p, s); break;
+        case GEMM_F32_ALGO_TILED: err = gemmf32::launch_tiled(p, s); break;
+        case GEMM_F32_ALGO_FMA: err = gemmf32::launch_fma(p, s); break;
+        case GEMM_F32_ALGO_MFMA:
+        case GEMM_F32_ALGO_AUTO:
+        default: err = gemmf32::launch_mfma(p, s); break;
+        }
+    }
+    return err == hipSuccess ? 0 : int(err);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+             const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
+             int transB, void *stream)
+{
+    return run(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream,
+               GEMM_F32_ALGO_AUTO);
+}
+
+int gemm_f32_naive(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                   const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
+                   int transB, void *stream)
+{
+    return run(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream,
+               GEMM_F32_ALGO_NAIVE);
+}
+
+int gemm_f32_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
+                int transB, void *stream, int algo)
+{
+    return run(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream, algo);
+}
+
+const char *gemm_f32_strerror(int status)
+{
+    switch (status) {
+    case 0: return "success";
+    case -kArgM: return "invalid argument 1 (M): negative or >= 2^31";
+    case -kArgN: return "invalid argument 2 (N): negative or >= 2^31";
+    case -kArgK: return "invalid argument 3 (K): negative or >= 2^31";
+    case -kArgA: return "invalid argument 4 (A): NULL with M*K > 0";
+    case -kArgLda: return "invalid argument 5 (lda): smaller than a stored row of A, or >= 2^31";
+    case -kArgB: return "invalid argument 6 (B): NULL with K*N > 0";
+    case -kArgLdb: return "invalid argument 7 (ldb): smaller than a stored row of B, or >= 2^31";
+    case -kArgC: return "invalid argument 8 (C): NULL with M*N > 0";
+    case -kArgLdc: return "invalid argument 9 (ldc): smaller than N, or >= 2^31";
+    case -kArgTransA: return "invalid argument 10 (transA): not 0 or 1";
+    case -kArgTransB: return "invalid argument 11 (transB): not 0 or 1";
+    case -kArgAlgo: return "invalid argument 13 (algo): unknown kernel family";
+    default: break;
+    }
+    if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
+    return "unknown status";
+}
+
+int gemm_f32_version(void) { return 10000; }
+
+}  // extern "C"

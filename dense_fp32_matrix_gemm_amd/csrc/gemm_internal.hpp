@@ -1,0 +1,47 @@
+// gemm_internal.hpp -- declarations shared by the host API and the kernel
+// translation units of the FP32 GEMM library.  Not installed; the public
+// interface is include/gemm_f32.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace gemmf32 {
+
+// A validated problem.  Dimensions fit in 31 bits (the API rejects larger);
+// leading dimensions are kept 64-bit so row offsets never overflow.
+struct Problem {
+    int M, N, K;
+    const float *A;
+    int64_t lda;
+    const float *B;
+    int64_t ldb;
+    float *C;
+    int64_t ldc;
+    int transA, transB;
+};
+
+// Each launcher enqueues its kernel(s) on `stream` and returns
+// hipGetLastError() after the launch.  All assume M, N, K >= 1.
+hipError_t launch_naive(const Problem &p, hipStream_t stream);
+hipError_t launch_tiled(const Problem &p, hipStream_t stream);
+hipError_t launch_fma(const Problem &p, hipStream_t stream);
+hipError_t launch_mfma(const Problem &p, hipStream_t stream);
+// C := 0 over M x N (the empty sum, K == 0).  Assumes M, N >= 1.
+hipError_t launch_zero_fill(const Problem &p, hipStream_t stream);
+
+// Number of 32-bit words per 16-byte vector.
+constexpr int kVec = 4;
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// True if every float4 this operand's vector loads touch is 16-byte aligned:
+// the base pointer is 16-byte aligned and the leading dimension is a
+// multiple of four floats.
+inline bool vec4_ok(const float *ptr, int64_t ld)
+{
+    return (reinterpret_cast<uintptr_t>(ptr) % 16 == 0) && (ld % kVec == 0);
+}
+
+}  // namespace gemmf32

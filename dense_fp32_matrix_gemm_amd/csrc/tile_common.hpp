@@ -1,0 +1,95 @@
+// tile_common.hpp -- device helpers shared by the LDS-tiled kernels (MFMA
+// and vector-FMA): the operand view, the coalesced global -> register
+// slice loader with zero-filled edges, and the XCD-aware tile order.
+#pragma once
+
+#include "gemm_internal.hpp"
+
+namespace gemmf32 {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// One operand as stored in global memory: a rows_total x cols_total
+// row-major matrix with leading dimension ld.  For A untransposed the rows
+// are m and the columns k; transposed, the rows are k and the columns m
+// (likewise for B with n).
+struct Operand {
+    const float *base;
+    int64_t ld;
+    int rows_total, cols_total;
+};
+
+// A ROWS x COLS slice of an operand, read as 16-byte vectors along the
+// contiguous direction.  Vector v of the slice (row v / (COLS/4), columns
+// 4 * (v % (COLS/4)) .. +3) is handled by thread v % THREADS, as the
+// per-thread index q = v / THREADS.  Consecutive threads therefore read
+// consecutive 16-byte pieces of a row: a 64-lane wave reads whole rows.
+template <int ROWS, int COLS, int THREADS>
+struct Slice {
+    static constexpr int vec_per_row = COLS / 4;
+    static constexpr int per_thread = ROWS * vec_per_row / THREADS;
+    static_assert(COLS % 4 == 0, "slice rows are whole vectors");
+    static_assert(ROWS * vec_per_row % THREADS == 0, "slice splits evenly over the block");
+
+    __device__ static __forceinline__ int row(int q) { return (int(threadIdx.x) + THREADS * q) / vec_per_row; }
+    __device__ static __forceinline__ int col(int q) { return ((int(threadIdx.x) + THREADS * q) % vec_per_row) * 4; }
+
+    // Load the slice whose stored origin is (r0, c0).  CHECK: elements
+    // outside rows_total x cols_total read as zero and are never
+    // dereferenced.  VEC: the operand allows aligned 16-byte loads
+    // (vec4_ok); otherwise each element is loaded on its own.
+    template <bool CHECK, bool VEC>
+    __device__ static __forceinline__ void load(const Operand &op, int r0, int c0, v4f (&reg)[per_thread])
+    {
+#pragma unroll
+        for (int q = 0; q < per_thread; ++q) {
+            const int r = r0 + row(q);
+            const int c = c0 + col(q);
+            const float *src = op.base + int64_t(r) * op.ld + c;
+            if (!CHECK) {
+                if (VEC) {
+                    reg[q] = *reinterpret_cast<const v4f *>(src);
+                } else {
+                    reg[q] = v4f{src[0], src[1], src[2], src[3]};
+                }
+            } else {
+                const bool row_ok = r < op.rows_total;
+                if (VEC && row_ok && c + 3 < op.cols_total) {
+                    reg[q] = *reinterpret_cast<const v4f *>(src);
+                } else {
+                    v4f x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = (row_ok && c + e < op.cols_total) ? src[e] : 0.0f;
+                    reg[q] = x;
+                }
+            }
+        }
+    }
+};
+
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+// Workgroup index -> (tile row, tile column) of a tiles_m x tiles_n grid.
+// Step 1 inverts the round-robin dealing of consecutive workgroups to the
+// XCDs, so that XCD x owns one contiguous range of the remapped index w.
+// Step 2 walks w GROUP_M tile-rows at a time, down each column of the
+// group before moving right, so the workgroups resident on one XCD at the
+// same time cover a compact block of C and share A and B panels in its L2.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int tiles = tiles_m * tiles_n;
+    const int q = tiles / kXcds, r = tiles % kXcds;
+    const int xcd = bid % kXcds, slot = bid / kXcds;
+    const int w = (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+    const int per_group = GROUP_M * tiles_n;
+    const int first = (w / per_group) * GROUP_M;
+    const int gm = min(tiles_m - first, GROUP_M);
+    const int local = w % per_group;
+    tm = first + local % gm;
+    tn = local / gm;
+}
+
+constexpr int kMaxGrid = 1 << 20;  // grid cap; tiled kernels stride over the rest
+
+}  // namespace gemmf32

@@ -1,0 +1,106 @@
+/*
+ * gemm_f32.h -- FP32 dense matrix multiply for AMD Instinct MI355X (gfx950).
+ *
+ *     C[M x N] = op(A)[M x K] . op(B)[K x N]          (FP32 in, FP32 out)
+ *
+ * The operation is the matrix product the course page "3 . La memoire
+ * partagee" builds up to in sections 3.1-3.4 (naive kernel, tiled kernel,
+ * register tiles), taken rectangular and row-major as in the cuda-oxide
+ * book's tiled_sgemm (page "shared memory and synchronisation"), with
+ * leading dimensions and optional transposes added so that the backward
+ * products of a training step need no transpose copies (the Smallem page,
+ * "Rendre le GPU rapide", section on the comparison with PyTorch, names
+ * transpose copies as a cost).
+ *
+ * Storage (all row-major, element (r, c) of a stored matrix at ptr[r*ld + c]):
+ *   transA == 0: A is stored M x K, element opA(i,k) = A[i*lda + k], lda >= max(1,K)
+ *   transA == 1: A is stored K x M, element opA(i,k) = A[k*lda + i], lda >= max(1,M)
+ *   transB == 0: B is stored K x N, element opB(k,j) = B[k*ldb + j], ldb >= max(1,N)
+ *   transB == 1: B is stored N x K, element opB(k,j) = B[j*ldb + k], ldb >= max(1,K)
+ *   C is stored M x N, C[i*ldc + j], ldc >= max(1,N).  C is overwritten
+ *   (there is no alpha/beta); elements of the padding (columns N..ldc-1) are
+ *   never written, and elements of A/B outside the used region are never
+ *   folded into the result (their values, NaN included, do not matter).
+ *
+ * Pointers and ownership: A, B and C are DEVICE pointers owned by the caller.
+ * The library allocates, frees and copies nothing, keeps no state between
+ * calls and never synchronises: each call enqueues its kernels on `stream`
+ * (a hipStream_t passed as void*; NULL means the default stream) and
+ * returns; C is complete when the stream reaches that point.  C must not
+ * overlap A or B.  Concurrent calls on different streams are safe.
+ *
+ * Arithmetic: products and sums in FP32 (IEEE round-to-nearest-even,
+ * fused multiply-add allowed).  The summation order over k is not the
+ * plain sequential one: partial sums over short runs of k are formed first
+ * and then added together, which bounds the rounding error growth for long
+ * K.  Any order is a correct evaluation of the product; results agree with
+ * an exact product to within 1e-6*K + 1e-5*|C| elementwise for inputs of
+ * magnitude <= 1.
+ *
+ * Return value (all entry points):
+ *     0   success (also for the quick returns below)
+ *    -i   the i-th argument (1-based, in the order of the prototype) is
+ *         invalid: M/N/K < 0 (-1/-2/-3); A NULL while M*K > 0 (-4); lda too
+ *         small (-5); B NULL while K*N > 0 (-6); ldb too small (-7); C NULL
+ *         while M*N > 0 (-8); ldc too small (-9); transA/transB not 0 or 1
+ *         (-10/-11); algo unknown (-13, gemm_f32_ex only); a dimension or
+ *         leading dimension >= 2^31 is reported as invalid for that
+ *         argument.  Validation is done on the host before any HIP call,
+ *         so these codes are returned even on a machine without a GPU.
+ *    >0   a hipError_t reported by the kernel launch (hipGetLastError()
+ *         is checked after every launch).
+ * Quick returns: M == 0 or N == 0 enqueues nothing; K == 0 writes C = 0
+ * (the empty sum) over the M x N region.
+ */
+#ifndef GEMM_F32_H
+#define GEMM_F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Kernel families selectable through gemm_f32_ex. */
+enum gemm_f32_algo {
+    GEMM_F32_ALGO_AUTO = 0,  /* the fastest path for the shape: currently MFMA */
+    GEMM_F32_ALGO_MFMA = 1,  /* LDS-staged tiles, FP32 matrix-core MFMA micro-tiles */
+    GEMM_F32_ALGO_FMA = 2,   /* LDS-staged tiles, register-blocked vector FMA */
+    GEMM_F32_ALGO_TILED = 3, /* T x T LDS tiles, one output per thread (section 3.3) */
+    GEMM_F32_ALGO_NAIVE = 4  /* one lane per output, operands from global memory (3.1) */
+};
+
+/* C = op(A) . op(B) on the fastest path (GEMM_F32_ALGO_AUTO). */
+int gemm_f32(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             int transA, int transB, void *stream);
+
+/* The naive baseline of section 3.1 of the course page: one lane per
+ * element of C, each lane reading its row of op(A) and column of op(B)
+ * straight from global memory.  Same contract as gemm_f32. */
+int gemm_f32_naive(int64_t M, int64_t N, int64_t K,
+                   const float *A, int64_t lda,
+                   const float *B, int64_t ldb,
+                   float *C, int64_t ldc,
+                   int transA, int transB, void *stream);
+
+/* gemm_f32 with an explicit kernel family (enum gemm_f32_algo). */
+int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc,
+                int transA, int transB, void *stream, int algo);
+
+/* A static, human-readable description of a return value (never NULL). */
+const char *gemm_f32_strerror(int status);
+
+/* Library interface version: major * 10000 + minor * 100 + patch. */
+int gemm_f32_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F32_H */

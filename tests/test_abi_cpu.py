@@ -1,0 +1,140 @@
+"""The C ABI on the host: symbols, argument validation, Python-side layout logic.
+
+CPU only: no test here launches a kernel.  Invalid arguments are rejected on
+the host before any HIP call, so the codes are checked without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_fp32_matrix_gemm_amd as g
+from dense_fp32_matrix_gemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+BIG = 1 << 31
+FAKE = 0x1000  # a non-NULL pointer value; never dereferenced by these tests
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b(\w+)\s*\(", text, flags=re.M):
+            if not m.group(0).lstrip().startswith(("#", "typedef", "enum", "struct")):
+                names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert {"gemm_f32", "gemm_f32_naive", "gemm_f32_ex", "gemm_f32_strerror",
+            "gemm_f32_version"} <= names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+    assert set(_lib.SIGNATURES) == declared_functions()
+
+
+def test_version(lib):
+    assert g.gemm_f32_version() == 10000
+
+
+def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
+         ta=0, tb=0, fn="gemm_f32", algo=None):
+    lda = max(1, M if ta else K) if lda is None else lda
+    ldb = max(1, K if tb else N) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    args = [M, N, K, A, lda, B, ldb, C, ldc, ta, tb, None]
+    if fn == "gemm_f32_ex":
+        args.append(0 if algo is None else algo)
+    return getattr(g, fn)(*args)
+
+
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_naive", "gemm_f32_ex"])
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(M=-1), -1), (dict(N=-1), -2), (dict(K=-1), -3),
+    (dict(M=BIG), -1), (dict(N=BIG), -2), (dict(K=BIG), -3),
+    (dict(A=None), -4), (dict(lda=3), -5), (dict(lda=BIG), -5),
+    (dict(B=None), -6), (dict(ldb=3), -7),
+    (dict(C=None), -8), (dict(ldc=3), -9), (dict(ldc=BIG), -9),
+    (dict(ta=2), -10), (dict(tb=-1), -11),
+    (dict(ta=1, lda=3, M=4, K=9), -5),      # transposed A: lda >= M
+    (dict(tb=1, ldb=8, K=9), -7),           # transposed B: ldb >= K
+    (dict(M=0, lda=0), -5),                 # lda >= 1 even when nothing is read
+])
+def test_invalid_arguments(fn, kwargs, code):
+    assert call(fn=fn, **kwargs) == code
+    assert g.gemm_f32_strerror(code).startswith(f"invalid argument {-code} ")
+
+
+def test_invalid_algo():
+    assert call(fn="gemm_f32_ex", algo=5) == -13
+    assert call(fn="gemm_f32_ex", algo=-1) == -13
+
+
+@pytest.mark.parametrize("kwargs", [dict(M=0, A=None, C=None), dict(N=0, B=None, C=None),
+                                    dict(M=0, N=0, A=None, B=None, C=None)])
+def test_quick_return_without_launch(kwargs):
+    """M == 0 or N == 0: nothing to write, status 0, no HIP call (works without a GPU)."""
+    assert call(**kwargs) == 0
+    assert call(fn="gemm_f32_ex", algo=1, **kwargs) == 0
+
+
+def test_strerror_is_total():
+    for st in range(-20, 1):
+        assert isinstance(g.gemm_f32_strerror(st), str)
+    assert g.gemm_f32_strerror(0) == "success"
+    assert g.gemm_f32_strerror(-99) == "unknown status"
+    assert len(g.gemm_f32_strerror(100)) > 0   # a hipError_t, described by HIP
+
+
+def test_launch_without_gpu_returns_hip_error():
+    """Valid arguments on a host with no GPU: a positive hipError_t, not a crash."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; this case is for GPU-less hosts")
+    st = call(M=2, N=2, K=2)
+    assert st > 0
+    assert isinstance(g.gemm_f32_strerror(st), str)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setenv("GEMM_F32_LIBRARY", str(tmp_path / "nope.so"))
+    with pytest.raises(_lib.LibraryNotBuilt):
+        _lib.load()
+
+
+def test_operand_layout_from_strides():
+    import torch
+    x = torch.empty(6, 10)
+    assert g.operand_layout(x) == (0, 10)
+    assert g.operand_layout(x.t()) == (1, 10)               # 10 x 6 view of a 6 x 10 array
+    assert g.operand_layout(x[:, :7]) == (0, 10)            # column slice keeps ld
+    assert g.operand_layout(x[:, :7].t()) == (1, 10)
+    with pytest.raises(ValueError):
+        g.operand_layout(x[:, ::2])
+
+
+def test_header_is_plain_c():
+    """The public header compiles as C with no HIP headers on the include path."""
+    import subprocess
+    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10000 ? 0 : 1;}\n"
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
