@@ -166,8 +166,8 @@ def copy_probe(mib: int = 1024, reps: int = 5) -> None:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "fma", "tiled", "naive"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
