@@ -27,7 +27,8 @@ struct Problem {
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_tiled(const Problem &p, hipStream_t stream);
 hipError_t launch_fma(const Problem &p, hipStream_t stream);
-hipError_t launch_mfma(const Problem &p, hipStream_t stream);
+// tile: 0 chooses by problem size; 128 or 64 forces that tile edge.
+hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
 // C := 0 over M x N (the empty sum, K == 0).  Assumes M, N >= 1.
 hipError_t launch_zero_fill(const Problem &p, hipStream_t stream);
 

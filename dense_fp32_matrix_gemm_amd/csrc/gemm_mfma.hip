@@ -48,11 +48,26 @@ namespace gemmf32 {
 namespace {
 
 template <bool V>
-struct integral_constant {
+struct Bool {
     static constexpr bool value = V;
 };
-using Yes = integral_constant<true>;
-using No = integral_constant<false>;
+template <int V>
+struct Int {
+    static constexpr int value = V;
+};
+using Yes = Bool<true>;
+using No = Bool<false>;
+
+// f(Int<0>{}), f(Int<1>{}), ..., f(Int<N-1>{}): a loop unrolled with the
+// index as a compile-time constant.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void unroll_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(Int<I>{});
+        unroll_for<N, I + 1>(f);
+    }
+}
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -65,12 +80,26 @@ constexpr int kBlk = 32;  // MFMA output block edge
 // waves per SIMD requested from the register allocator, GROUP_M tile-rows
 // per group in the launch order, and WRITE_G, the k group of a stage after
 // whose fragment reads register-staged data for the next stage is written
-// to LDS (BK / 8 means after the last group).
+// to LDS (BK / 8 means after the last group), and CHAINS, the number of
+// independent partial sums each block keeps within a stage (MFMA u of a k
+// group feeds chain u % CHAINS).  One chain suffices when a wave owns
+// several blocks; a wave with a single block needs more than one to keep
+// consecutive MFMAs independent.  KSPLIT > 1 splits every stage's k groups
+// over KSPLIT slices of WAVES_M x WAVES_N waves (slice s takes groups s,
+// s + KSPLIT, ...); each slice accumulates its own partial tile and the
+// slices are summed through LDS at the end.  It gives small grids more
+// waves per SIMD without any memory outside the output.  NBUF stage
+// buffers let the copy of stage s + NBUF - 1 run while stage s is computed;
+// FOLD stages form one accumulation chunk on that path.
 template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int WPE_, int GROUP_M_,
-          int WRITE_G_>
+          int WRITE_G_, int CHAINS_, int KSPLIT_, int NBUF_, int FOLD_>
 struct Config {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
-    static constexpr int waves = WAVES_M * WAVES_N;
+    static constexpr int nbuf = NBUF_;  // LDS stage buffers (copies in flight: NBUF - 1)
+    static constexpr int fold = FOLD_;  // stages per accumulation chunk on the copy path
+    static constexpr int ksplit = KSPLIT_;                 // k-slices of waves
+    static constexpr int waves_mn = WAVES_M * WAVES_N;     // waves per k-slice
+    static constexpr int waves = waves_mn * KSPLIT_;
     static constexpr int threads = kWave * waves;
     static constexpr int waves_n = WAVES_N;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -78,8 +107,15 @@ struct Config {
     static constexpr int wpe = WPE_;
     static constexpr int group_m = GROUP_M_;
     static constexpr int write_g = WRITE_G_;
+    static constexpr int chains = CHAINS_;  // independent partial sums per block
+    static_assert(4 % CHAINS_ == 0, "chains divide the 4 MFMAs of a k group");
     static_assert(WM % kBlk == 0 && WN % kBlk == 0, "wave tiles are whole MFMA blocks");
     static_assert(BK % 8 == 0, "stages are whole 8-k fragment groups");
+    static_assert((BK / 8) % KSPLIT_ == 0, "k-slices share a stage's groups evenly");
+    static_assert(KSPLIT_ == 1 || KSPLIT_ == 2 || KSPLIT_ == 4, "k-slices reduce as a binary tree");
+    static_assert(NBUF_ >= 2 && NBUF_ <= 4 && NBUF_ % FOLD_ == 0, "2-4 stage buffers, whole chunks");
+    static_assert(KSPLIT_ == 1 || BM * BN <= (BM + BN) * BK,
+                  "a k-slice's partial tile fits in one stage buffer for the reduction");
 };
 
 // LDS tile of one operand for one stage.  P = extent along m (or n); KC =
@@ -94,8 +130,14 @@ struct Tile {
     static constexpr int vpr = cols / 4;  // 16-byte vectors per row
     static constexpr int floats = rows * cols;
     static constexpr int chunks = rows * vpr / kWave;  // 1 KB pieces, one per DMA instruction
-    static constexpr int dma_per_wave = chunks / Cfg::waves;
-    static_assert(chunks % Cfg::waves == 0, "DMA instructions split evenly over the waves");
+    static constexpr int dma_per_wave = (chunks + Cfg::waves - 1) / Cfg::waves;
+    static_assert(chunks % Cfg::waves == 0 || Cfg::waves % chunks == 0,
+                  "DMA instructions split evenly over the waves, or over the first waves");
+    // False only for the waves past the last piece when pieces < waves.
+    __device__ static __forceinline__ bool dma_active(int wave, int q)
+    {
+        return chunks % Cfg::waves == 0 || wave * dma_per_wave + q < chunks;
+    }
     static_assert((vpr & (vpr - 1)) == 0, "rows hold a power-of-two number of vectors");
     using Load = Slice<rows, cols, Cfg::threads>;
     static constexpr int per_thread = Load::per_thread;
@@ -109,9 +151,15 @@ struct Tile {
     //   (lanes 0-31) and of row k + 4 (lanes 32-63); flipping bit 3 of the
     //   vector index every 4 rows puts the two halves in opposite 128-byte
     //   halves of a 256-byte bank line.
+    //   With 4 vectors per row (BK = 16) the same two properties come from
+    //   ((r >> 1) ^ (r >> 2)) & 3.
     __device__ static __forceinline__ int swz(int r)
     {
-        return KC ? (((r & 7) ^ ((r >> 3) & 1)) & (vpr - 1)) : ((((r >> 2) & 1) << 3) & (vpr - 1));
+        if (KC) {
+            if (vpr == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+            return ((r & 7) ^ ((r >> 3) & 1)) & (vpr - 1);
+        }
+        return (((r >> 2) & 1) << 3) & (vpr - 1);
     }
     __device__ static __forceinline__ int slot(int r, int v) { return r * vpr + (v ^ swz(r)); }
 
@@ -121,7 +169,8 @@ struct Tile {
     {
 #pragma unroll
         for (int q = 0; q < per_thread; ++q)
-            *reinterpret_cast<v4f *>(lds + 4 * slot(Load::row(q), Load::col(q) / 4)) = reg[q];
+            if (Load::active(q))
+                *reinterpret_cast<v4f *>(lds + 4 * slot(Load::row(q), Load::col(q) / 4)) = reg[q];
     }
 
     // Byte offset, from the stage's stored origin, of the vector this lane
@@ -142,8 +191,9 @@ struct Tile {
     {
 #pragma unroll
         for (int q = 0; q < dma_per_wave; ++q)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(origin + off[q]),
-                                             lds + (wave * dma_per_wave + q) * 256, 16, 0, 0);
+            if (dma_active(wave, q))
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(origin + off[q]),
+                                                 lds + (wave * dma_per_wave + q) * 256, 16, 0, 0);
     }
 
     // The four k values (one per MFMA u = 0..3) this lane feeds for k group
@@ -160,8 +210,16 @@ struct Tile {
     }
 };
 
-// Wait until this wave's global->LDS copies have landed.
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+// Wait until at most N of this wave's vector-memory operations (here: the
+// global->LDS copies) are outstanding; they complete in issue order.
+// gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8
+// left at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 template <class Cfg, bool A_KC, bool B_KC, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::threads, Cfg::threads),
@@ -174,17 +232,21 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     constexpr int FM = Cfg::FM, FN = Cfg::FN;
     using TA = Tile<Cfg, BM, A_KC>;
     using TB = Tile<Cfg, BN, B_KC>;
-    // Two stage buffers as separate objects, so the compiler can tell a
-    // copy into one from reads of the other.
-    __shared__ __attribute__((aligned(1024))) float buf0[TA::floats + TB::floats];
-    __shared__ __attribute__((aligned(1024))) float buf1[TA::floats + TB::floats];
+    // Stage buffers as separate objects, so the compiler can tell a copy into
+    // one from reads of another.
+    constexpr int kStage = TA::floats + TB::floats;
+    __shared__ __attribute__((aligned(1024))) float buf0[kStage];
+    __shared__ __attribute__((aligned(1024))) float buf1[kStage];
+    __shared__ __attribute__((aligned(1024))) float buf2[Cfg::nbuf > 2 ? kStage : 1];
+    __shared__ __attribute__((aligned(1024))) float buf3[Cfg::nbuf > 3 ? kStage : 1];
 
     int tm, tn;
     tile_of<Cfg::group_m>(tile_base + int(blockIdx.x), tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const bool inside = (m0 + BM <= M) && (n0 + BN <= N);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int wm = (wave / Cfg::waves_n) * Cfg::WM, wn = (wave % Cfg::waves_n) * Cfg::WN;
+    const int kslice = wave / Cfg::waves_mn, wmn = wave % Cfg::waves_mn;
+    const int wm = (wmn / Cfg::waves_n) * Cfg::WM, wn = (wmn % Cfg::waves_n) * Cfg::WN;
     const int half = lane / 32, l32 = lane % 32;
     const int stages = ceil_div(K, BK);
     const int full = K / BK;  // stages that lie entirely inside K
@@ -200,33 +262,50 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     // write_g (the register-staged path writes the next stage there; the
     // buffer it writes was last read in the previous stage, which every wave
     // finished before that stage's barrier).
-    auto compute = [&](const float *lds, auto mid) {
+    constexpr int CH = Cfg::chains;
+    v16f part[CH][FM][FN];
+    auto fold_part = [&] {
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] += part[c][i][j];
+    };
+    // MFMAs over the BK k values in `lds` into the partial tile; FRESH starts
+    // a chunk (the first MFMA of each chain takes a zero addend), FOLD ends
+    // it (the partial tile is added into acc).  `mid` runs after the
+    // fragment reads of k group write_g (the register-staged path writes the
+    // next stage there; the buffer it writes was last read in the previous
+    // stage, which every wave finished before that stage's barrier).
+    auto compute = [&](const float *lds, auto mid, auto fresh_t, auto fold_t) {
+        constexpr bool kFresh = decltype(fresh_t)::value;
+        constexpr bool kFold = decltype(fold_t)::value;
         const float *la = lds;
         const float *lb = lds + TA::floats;
-        v16f part[FM][FN];
+        constexpr int kGroups = BK / 8 / Cfg::ksplit;  // k groups per slice per stage
 #pragma unroll
-        for (int g = 0; g < BK / 8; ++g) {
+        for (int t = 0; t < kGroups; ++t) {
+            const int g = Cfg::ksplit == 1 ? t : t * Cfg::ksplit + kslice;
             v4f fa[FM], fb[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i) fa[i] = TA::fragment(la, wm + i * kBlk + l32, g, half);
 #pragma unroll
             for (int j = 0; j < FN; ++j) fb[j] = TB::fragment(lb, wn + j * kBlk + l32, g, half);
-            if (g == Cfg::write_g) mid();
+            if (Cfg::ksplit == 1 && t == Cfg::write_g) mid();
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        part[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            fa[i][u], fb[j][u], (g == 0 && u == 0) ? v16f{0.0f} : part[i][j], 0, 0,
-                            0);
+                    for (int j = 0; j < FN; ++j) {
+                        v16f &p = part[u % CH][i][j];
+                        p = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            fa[i][u], fb[j][u], (kFresh && t == 0 && u < CH) ? v16f{0.0f} : p, 0, 0, 0);
+                    }
         }
-        if (Cfg::write_g >= BK / 8) mid();
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] += part[i][j];
+        if (Cfg::ksplit > 1 || Cfg::write_g >= kGroups) mid();
+        if (kFold) fold_part();
     };
     auto nothing = [] {};
 
@@ -251,16 +330,16 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                 compute(cur, [&] {
                     TA::store(nxt, ra);
                     TB::store(nxt + TA::floats, rb);
-                });
+                }, Yes{}, Yes{});
             } else {
-                compute(cur, nothing);
+                compute(cur, nothing, Yes{}, Yes{});
             }
             __syncthreads();
         }
     };
 
     if (VEC && dma_ok && inside && full >= 1) {
-        // Interior tile: full stages copied straight into LDS, one ahead.
+        // Interior tile: full stages copied straight into LDS, NBUF - 1 ahead.
         uint32_t oa[TA::dma_per_wave], ob[TB::dma_per_wave];
 #pragma unroll
         for (int q = 0; q < TA::dma_per_wave; ++q) oa[q] = TA::dma_offset(lda, wave, lane, q);
@@ -272,35 +351,56 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         const char *gb = reinterpret_cast<const char *>(B + int64_t(b_r(0)) * ldb + b_c(0));
         const int64_t a_step = 4 * (A_KC ? int64_t(BK) : int64_t(BK) * lda);
         const int64_t b_step = 4 * (B_KC ? int64_t(BK) : int64_t(BK) * ldb);
+        constexpr int NB = Cfg::nbuf, FOLD = Cfg::fold;
+        // Copies per wave per stage; every wave issues the same number, so a
+        // count of outstanding copies names a stage.
+        constexpr int D = TA::dma_per_wave + TB::dma_per_wave;
+        static_assert(NB == 2 || (TA::chunks % Cfg::waves == 0 && TB::chunks % Cfg::waves == 0),
+                      "deeper pipelines need the same copy count on every wave");
+        auto bufp = [&](auto idx) -> float * {
+            constexpr int I = decltype(idx)::value;
+            return I == 0 ? buf0 : I == 1 ? buf1 : I == 2 ? buf2 : buf3;
+        };
         auto dma = [&](float *lds, int stage) {
             TA::dma(lds, ga + stage * a_step, oa, wave);
             TB::dma(lds + TA::floats, gb + stage * b_step, ob, wave);
         };
         dma(buf0, 0);
-        wait_dma();
-        __syncthreads();
-        int s = 0;
-        // Two stages per trip so each buffer is a compile-time choice.
-        for (; s + 2 < full; s += 2) {
-            dma(buf1, s + 1);
-            compute(buf0, nothing);
-            wait_dma();
+        if (NB > 2 && 1 < full) dma(bufp(Int<1 % NB>{}), 1);
+        if (NB > 3 && 2 < full) dma(bufp(Int<2 % NB>{}), 2);
+        // NB stages per trip so each buffer is a compile-time choice.
+        for (int s = 0; s < full; s += NB) {
+            unroll_for<NB>([&](auto bi) {
+                constexpr int b = decltype(bi)::value;
+                const int st = s + b;
+                if (st < full) {
+                    // Stage st has landed (at most the copies of the NB - 2
+                    // later stages are outstanding); after the barrier every
+                    // wave's share is visible, and every wave is done with
+                    // stage st - 1, whose buffer the next copy refills.
+                    if (NB == 2 || st + NB - 2 >= full)
+                        wait_vm<0>();
+                    else
+                        wait_vm<(NB - 2) * D>();
+                    __syncthreads();
+                    if (st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
+                    compute(bufp(Int<b>{}), nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{});
+                }
+            });
+        }
+        if (full % FOLD != 0) fold_part();  // the last chunk was cut short
+        __syncthreads();  // every wave is done with the last full stage's buffer
+        if (full < stages) {
+            // The partial last stage, predicated, through registers.
+            v4f ra[TA::per_thread], rb[TB::per_thread];
+            TA::Load::template load<true, VEC>(opa, a_r(full * BK), a_c(full * BK), ra);
+            TB::Load::template load<true, VEC>(opb, b_r(full * BK), b_c(full * BK), rb);
+            TA::store(buf0, ra);
+            TB::store(buf0 + TA::floats, rb);
             __syncthreads();
-            dma(buf0, s + 2);
-            compute(buf1, nothing);
-            wait_dma();
+            compute(buf0, nothing, Yes{}, Yes{});
             __syncthreads();
         }
-        if (s + 1 < full) {
-            dma(buf1, s + 1);
-            compute(buf0, nothing);
-            wait_dma();
-            __syncthreads();
-            ++s;
-        }
-        // Stage s, the last full one, is in buffer s & 1; a partial stage
-        // after it, if any, goes through the predicated path.
-        staged(s);
     } else {
         v4f ra[TA::per_thread], rb[TB::per_thread];
         TA::Load::template load<true, VEC>(opa, a_r(0), a_c(0), ra);
@@ -309,6 +409,39 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         TB::store(buf0 + TA::floats, rb);
         __syncthreads();
         staged(0);
+    }
+
+    // Sum the k-slices' partial tiles, pairwise through the (now idle)
+    // stage buffers: at each level the upper half of the slices writes, the
+    // lower half adds.  Every stage buffer holds at least one BM x BN tile.
+    if (Cfg::ksplit > 1) {
+#pragma unroll
+        for (int width = Cfg::ksplit / 2; width >= 1; width /= 2) {
+            const bool writer = kslice >= width && kslice < 2 * width;
+            const bool reader = kslice < width;
+            float *xbuf = ((kslice % width) == 0) ? buf0 : buf1;  // width <= 2
+            if (writer) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            xbuf[(((wmn * FM + i) * FN + j) * 16 + v) * kWave + lane] = acc[i][j][v];
+            }
+            __syncthreads();
+            if (reader) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            acc[i][j][v] += xbuf[(((wmn * FM + i) * FN + j) * 16 + v) * kWave + lane];
+            }
+            __syncthreads();
+        }
+        if (kslice != 0) return;  // slice 0 holds the sum; no barrier follows
     }
 
     // Epilogue.  Lane l of a 32 x 32 block holds column l % 32 and, in
@@ -327,9 +460,13 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 }
 
 #ifndef GEMM_MFMA_CONFIG
-#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3
+#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 1
+#endif
+#ifndef GEMM_MFMA_SMALL_CONFIG
+#define GEMM_MFMA_SMALL_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 1
 #endif
 using Default = Config<GEMM_MFMA_CONFIG>;
+using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
 
 // True if every DMA offset of an operand's stage fits in 32 bits.
 inline bool dma_offsets_fit(int rows, int64_t ld) { return (int64_t(rows) * ld + ld) * 4 < (int64_t(1) << 32); }
@@ -374,11 +511,25 @@ void dispatch_layout(const Problem &p, hipStream_t s)
     }
 }
 
+// The large tile needs about two workgroups per CU to keep the matrix cores
+// busy; below 256 large tiles (one per CU) the 64 x 64 tile, with each
+// stage's k groups split over two slices of waves, gives more parallelism.
+#ifndef GEMM_MFMA_SMALL_BELOW
+#define GEMM_MFMA_SMALL_BELOW 256
+#endif
+
 }  // namespace
 
-hipError_t launch_mfma(const Problem &p, hipStream_t s)
+hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
 {
-    dispatch_layout<Default>(p, s);
+    if (tile == 0) {
+        const int64_t big_tiles = int64_t(ceil_div(p.M, Default::BM)) * ceil_div(p.N, Default::BN);
+        tile = big_tiles < GEMM_MFMA_SMALL_BELOW ? Small::BM : Default::BM;
+    }
+    if (tile == Small::BM)
+        dispatch_layout<Small>(p, s);
+    else
+        dispatch_layout<Default>(p, s);
     return hipGetLastError();
 }
 

@@ -27,12 +27,17 @@ struct Operand {
 template <int ROWS, int COLS, int THREADS>
 struct Slice {
     static constexpr int vec_per_row = COLS / 4;
-    static constexpr int per_thread = ROWS * vec_per_row / THREADS;
+    static constexpr int vecs = ROWS * vec_per_row;
+    static constexpr int per_thread = (vecs + THREADS - 1) / THREADS;
     static_assert(COLS % 4 == 0, "slice rows are whole vectors");
-    static_assert(ROWS * vec_per_row % THREADS == 0, "slice splits evenly over the block");
+    static_assert(vecs % THREADS == 0 || THREADS % vecs == 0,
+                  "a slice splits evenly over the block, or covers part of it");
 
-    __device__ static __forceinline__ int row(int q) { return (int(threadIdx.x) + THREADS * q) / vec_per_row; }
-    __device__ static __forceinline__ int col(int q) { return ((int(threadIdx.x) + THREADS * q) % vec_per_row) * 4; }
+    __device__ static __forceinline__ int index(int q) { return int(threadIdx.x) + THREADS * q; }
+    // False only for the threads past the end of a slice smaller than the block.
+    __device__ static __forceinline__ bool active(int q) { return vecs % THREADS == 0 || index(q) < vecs; }
+    __device__ static __forceinline__ int row(int q) { return index(q) / vec_per_row; }
+    __device__ static __forceinline__ int col(int q) { return (index(q) % vec_per_row) * 4; }
 
     // Load the slice whose stored origin is (r0, c0).  CHECK: elements
     // outside rows_total x cols_total read as zero and are never
@@ -43,6 +48,10 @@ struct Slice {
     {
 #pragma unroll
         for (int q = 0; q < per_thread; ++q) {
+            if (!active(q)) {
+                reg[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                continue;
+            }
             const int r = r0 + row(q);
             const int c = c0 + col(q);
             const float *src = op.base + int64_t(r) * op.ld + c;

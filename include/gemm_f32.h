@@ -64,10 +64,13 @@ extern "C" {
 /* Kernel families selectable through gemm_f32_ex. */
 enum gemm_f32_algo {
     GEMM_F32_ALGO_AUTO = 0,  /* the fastest path for the shape: currently MFMA */
-    GEMM_F32_ALGO_MFMA = 1,  /* LDS-staged tiles, FP32 matrix-core MFMA micro-tiles */
+    GEMM_F32_ALGO_MFMA = 1,  /* LDS-staged tiles, FP32 matrix-core MFMA micro-tiles;
+                                the tile size is chosen from the problem size */
     GEMM_F32_ALGO_FMA = 2,   /* LDS-staged tiles, register-blocked vector FMA */
     GEMM_F32_ALGO_TILED = 3, /* T x T LDS tiles, one output per thread (section 3.3) */
-    GEMM_F32_ALGO_NAIVE = 4  /* one lane per output, operands from global memory (3.1) */
+    GEMM_F32_ALGO_NAIVE = 4, /* one lane per output, operands from global memory (3.1) */
+    GEMM_F32_ALGO_MFMA_TILE128 = 5, /* MFMA with the 128 x 128 tile forced */
+    GEMM_F32_ALGO_MFMA_TILE64 = 6   /* MFMA with the 64 x 64 (split-k-group) tile forced */
 };
 
 /* C = op(A) . op(B) on the fastest path (GEMM_F32_ALGO_AUTO). */

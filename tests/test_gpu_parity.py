@@ -12,8 +12,8 @@ import parity as P
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["mfma", "fma", "tiled", "naive"]
-FAST_ALGOS = ["mfma", "fma"]
+ALGOS = ["mfma", "mfma128", "mfma64", "fma", "tiled", "naive"]
+FAST_ALGOS = ["mfma128", "mfma64", "fma"]
 
 _ref_cache = {}
 
