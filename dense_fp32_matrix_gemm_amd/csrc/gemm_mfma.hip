@@ -460,10 +460,10 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 }
 
 #ifndef GEMM_MFMA_CONFIG
-#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 1
+#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 2
 #endif
 #ifndef GEMM_MFMA_SMALL_CONFIG
-#define GEMM_MFMA_SMALL_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 1
+#define GEMM_MFMA_SMALL_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4
 #endif
 using Default = Config<GEMM_MFMA_CONFIG>;
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
@@ -512,11 +512,19 @@ void dispatch_layout(const Problem &p, hipStream_t s)
 }
 
 // The large tile needs about two workgroups per CU to keep the matrix cores
-// busy; below 256 large tiles (one per CU) the 64 x 64 tile, with each
-// stage's k groups split over two slices of waves, gives more parallelism.
+// busy.  Below 256 large tiles (one per CU), or below 512 when K is short
+// enough that each tile's k loop cannot amortise its start-up, the 64 x 64
+// tile, with each stage's k groups split over two slices of waves, gives
+// more parallelism (measured: S1k 30 -> 88 TFLOP/s, the 2049 x 3071 x 769
+// ragged product 81 -> 86; the 1024 x 4096 x 8192 weight gradient, 256
+// large tiles, stays faster on the large tile).
 #ifndef GEMM_MFMA_SMALL_BELOW
 #define GEMM_MFMA_SMALL_BELOW 256
 #endif
+#ifndef GEMM_MFMA_SHORT_K_SMALL_BELOW
+#define GEMM_MFMA_SHORT_K_SMALL_BELOW 512
+#endif
+constexpr int kShortK = 1024;
 
 }  // namespace
 
@@ -524,7 +532,9 @@ hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
 {
     if (tile == 0) {
         const int64_t big_tiles = int64_t(ceil_div(p.M, Default::BM)) * ceil_div(p.N, Default::BN);
-        tile = big_tiles < GEMM_MFMA_SMALL_BELOW ? Small::BM : Default::BM;
+        const bool small = big_tiles < GEMM_MFMA_SMALL_BELOW ||
+                           (p.K <= kShortK && big_tiles < GEMM_MFMA_SHORT_K_SMALL_BELOW);
+        tile = small ? Small::BM : Default::BM;
     }
     if (tile == Small::BM)
         dispatch_layout<Small>(p, s);
