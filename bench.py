@@ -205,13 +205,25 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
     algo_id = g.ALGOS[args.algo]
 
+    batched = w.batch > 1
+    if batched and args.algo not in ("auto", "mfma"):
+        print("batched workloads run on the MFMA path only", file=sys.stderr)
+        return 2
+
     def step(algo=algo_id):
-        st = g.gemm_f32_ex(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
-                           dC.data_ptr(), w.ldc_, w.transA, w.transB, stream.cuda_stream, algo)
+        if batched:
+            st = g.gemm_f32_strided_batched(
+                w.M, w.N, w.K, dA.data_ptr(), w.lda_, w.stride_a, dB.data_ptr(), w.ldb_,
+                w.stride_b, dC.data_ptr(), w.ldc_, w.stride_c, w.batch, w.transA, w.transB,
+                stream.cuda_stream)
+        else:
+            st = g.gemm_f32_ex(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
+                               dC.data_ptr(), w.ldc_, w.transA, w.transB, stream.cuda_stream,
+                               algo)
         if st != 0:
             raise g.GemmError(st)
 
-    flops = gemm_flops(w.M, w.N, w.K)
+    flops = w.flops
     torch.cuda.synchronize()
     ms = _timed(step, args.steps, args.warmup)
     value = flops / (ms * 1e-3) / 1e12
@@ -221,8 +233,14 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         import oracle
         rows, cols = gi.sample_entries(w.M, w.N, 256, seed=23)
-        ref = oracle.load().entries(A, B, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
-        got = dC.cpu().numpy()[rows, cols].astype(np.float64)
+        a0, b0, c0 = A, B, dC.cpu().numpy()
+        if batched:  # the last product of the batch
+            last = w.batch - 1
+            a0 = A[last, :w.a_dims[0] * w.lda_].reshape(w.a_dims[0], w.lda_)
+            b0 = B if w.shared_b else B[last, :w.b_dims[0] * w.ldb_].reshape(w.b_dims[0], w.ldb_)
+            c0 = c0[last, :w.M * w.ldc_].reshape(w.M, w.ldc_)
+        ref = oracle.load().entries(a0, b0, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
+        got = c0[rows, cols].astype(np.float64)
         ratio = np.abs(got - ref) / (1e-6 * w.K + 1e-5 * np.abs(ref))
         parity = {"entries": int(rows.size), "max_err_over_bound": float(np.max(ratio)),
                   "ok": bool(np.all(ratio <= 1.0))}
@@ -232,7 +250,7 @@ def main(argv=None) -> int:
                 "unit": "TFLOP/s", "frac": value / MI355X_FP32_PEAK_TFLOPS,
                 "traffic": read_traffic(kernel, name),
                 "kernel": kernel, "flops_per_launch": flops,
-                "compulsory_bytes": compulsory_bytes(w.M, w.N, w.K)}
+                "compulsory_bytes": compulsory_bytes(w.M, w.N, w.K) * w.batch}
     if args.algo == "naive":
         model = naive_model_bytes(w.M, w.N, w.K) / (ms * 1e-3) / 1e9
         roofline.update(bound="hbm", achieved=model, peak=MI355X_HBM_TBPS * 1000,
@@ -241,7 +259,18 @@ def main(argv=None) -> int:
         roofline["bound"] = "alu"   # vector FP32 FMA; same 157.3 TFLOP/s peak as the matrix cores
 
     context = None
-    if not args.no_context:
+    if not args.no_context and batched:
+        def view(x, rows, cols, ld, stride, trans):
+            v = x[:, :rows * ld].reshape(-1, rows, ld)[:, :, :cols]
+            v = v.expand(w.batch, rows, cols) if stride == 0 else v
+            return (v.transpose(1, 2) if trans else v).contiguous()
+        ta = view(dA.reshape(-1, A.shape[-1]), *w.a_dims, w.lda_, w.stride_a, w.transA)
+        tb = view(dB.reshape(-1, B.shape[-1]), *w.b_dims, w.ldb_, w.stride_b, w.transB)
+        out = torch.empty((w.batch, w.M, w.N), dtype=torch.float32, device="cuda")
+        tms = _timed(lambda: torch.bmm(ta, tb, out=out), 10, 2)
+        context = {"torch.bmm (contiguous copies)": {"tflops": flops / (tms * 1e-3) / 1e12,
+                                                     "ms": tms}}
+    elif not args.no_context:
         context = {}
         for other in ("mfma", "fma", "tiled", "naive"):
             if other == args.algo or (other == "mfma" and args.algo == "auto"):
@@ -265,7 +294,7 @@ def main(argv=None) -> int:
         context["torch.mm"] = {"tflops": flops / (tms * 1e-3) / 1e12, "ms": tms}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not batched:
         cpu = cpu_baseline(w)
 
     line = {
@@ -281,7 +310,8 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda_,
+        "config": {"workload": name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
+                   "lda": w.lda_,
                    "ldb": w.ldb_, "ldc": w.ldc_, "transA": w.transA, "transB": w.transB,
                    "inputs": w.description, "seeds": [w.seed_a, w.seed_b],
                    "algo": args.algo, "parallelism": "single GPU"},

@@ -11,11 +11,12 @@ current stream, and calls the library.  PyTorch owns memory and streams.
 from __future__ import annotations
 
 from ._lib import (ALGOS, LibraryNotBuilt, gemm_f32, gemm_f32_ex, gemm_f32_naive,
-                   gemm_f32_strerror, gemm_f32_version, library_path, load)
+                   gemm_f32_strerror, gemm_f32_strided_batched, gemm_f32_version, library_path,
+                   load)
 
-__all__ = ["ALGOS", "GemmError", "LibraryNotBuilt", "gemm_f32", "gemm_f32_ex",
-           "gemm_f32_naive", "gemm_f32_strerror", "gemm_f32_version", "library_path",
-           "load", "matmul", "operand_layout"]
+__all__ = ["ALGOS", "GemmError", "LibraryNotBuilt", "bmm", "gemm_f32", "gemm_f32_ex",
+           "gemm_f32_naive", "gemm_f32_strerror", "gemm_f32_strided_batched",
+           "gemm_f32_version", "library_path", "load", "matmul", "operand_layout"]
 
 
 class GemmError(RuntimeError):
@@ -70,6 +71,41 @@ def matmul(a, b, out=None, algo: str = "auto", stream=None):
         stream = torch.cuda.current_stream(a.device).cuda_stream
     st = gemm_f32_ex(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
                      ta, tb, stream, ALGOS[algo])
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def bmm(a, b, out=None, stream=None):
+    """out[i] = a[i] @ b[i] for 3-D float32 device tensors, one strided-batched call.
+
+    ``a`` is (batch, M, K) and ``b`` is (batch, K, N); each may be a view with
+    its last two dimensions transposed (e.g. ``k.transpose(1, 2)``), mapped to
+    the transpose flag without a copy, and a batch stride of 0 (an expanded
+    operand) shares one matrix across the batch.
+    """
+    import torch
+
+    if a.dim() != 3 or b.dim() != 3:
+        raise ValueError("bmm operands are 3-D")
+    if a.dtype != torch.float32 or b.dtype != torch.float32:
+        raise TypeError("bmm takes float32 tensors")
+    batch, M, K = a.shape
+    if b.shape[0] != batch or b.shape[1] != K:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not chain")
+    N = b.shape[2]
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=torch.float32, device=a.device)
+    if out.shape != (batch, M, N) or (N > 1 and out.stride(2) != 1):
+        raise ValueError("out must be (batch, M, N) with unit column stride")
+    ta, lda = operand_layout(a[0]) if batch else (0, max(K, 1))
+    tb, ldb = operand_layout(b[0]) if batch else (0, max(N, 1))
+    ldc = max(out.stride(1), N, 1) if M > 1 else max(N, 1)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    st = gemm_f32_strided_batched(M, N, K, a.data_ptr(), lda, a.stride(0), b.data_ptr(), ldb,
+                                  b.stride(0), out.data_ptr(), ldc, out.stride(0), batch,
+                                  ta, tb, stream)
     if st != 0:
         raise GemmError(st)
     return out

@@ -25,6 +25,8 @@ SIGNATURES = {
     "gemm_f32": (_int, _GEMM_ARGS),
     "gemm_f32_naive": (_int, _GEMM_ARGS),
     "gemm_f32_ex": (_int, _GEMM_ARGS + [_int]),
+    "gemm_f32_strided_batched": (_int, [_i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64,
+                                        _ptr, _i64, _i64, _i64, _int, _int, _ptr]),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
     "gemm_f32_version": (_int, []),
 }
@@ -75,6 +77,12 @@ def gemm_f32_naive(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream) -> i
 
 def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream, algo) -> int:
     return _call("gemm_f32_ex", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream, algo)
+
+
+def gemm_f32_strided_batched(M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                             batch, transA, transB, stream) -> int:
+    return _call("gemm_f32_strided_batched", M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc,
+                 strideC, batch, transA, transB, stream)
 
 
 def gemm_f32_strerror(status: int) -> str:

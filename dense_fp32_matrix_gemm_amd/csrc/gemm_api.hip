@@ -20,9 +20,11 @@ enum Arg {
     kArgTransA, kArgTransB, kArgStream, kArgAlgo
 };
 
+// check_ptrs false: nothing will be read or written (an empty batch), so
+// the pointers may be anything.
 int validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
              const float *B, int64_t ldb, const float *C, int64_t ldc,
-             int transA, int transB)
+             int transA, int transB, bool check_ptrs = true)
 {
     if (M < 0 || M > kDimLimit) return -kArgM;
     if (N < 0 || N > kDimLimit) return -kArgN;
@@ -31,11 +33,11 @@ int validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     if (transB != 0 && transB != 1) return -kArgTransB;
     const int64_t a_row = transA ? M : K;   // length of a stored row of A
     const int64_t b_row = transB ? K : N;   // length of a stored row of B
-    if (A == nullptr && M * K > 0) return -kArgA;
+    if (check_ptrs && A == nullptr && M * K > 0) return -kArgA;
     if (lda < (a_row > 1 ? a_row : 1) || lda > kDimLimit) return -kArgLda;
-    if (B == nullptr && K * N > 0) return -kArgB;
+    if (check_ptrs && B == nullptr && K * N > 0) return -kArgB;
     if (ldb < (b_row > 1 ? b_row : 1) || ldb > kDimLimit) return -kArgLdb;
-    if (C == nullptr && M * N > 0) return -kArgC;
+    if (check_ptrs && C == nullptr && M * N > 0) return -kArgC;
     if (ldc < (N > 1 ? N : 1) || ldc > kDimLimit) return -kArgLdc;
     return 0;
 }
@@ -118,6 +120,36 @@ const char *gemm_f32_strerror(int status)
     return "unknown status";
 }
 
-int gemm_f32_version(void) { return 10000; }
+int gemm_f32_strided_batched(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                             int64_t strideA, const float *B, int64_t ldb, int64_t strideB,
+                             float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                             int transA, int transB, void *stream)
+{
+    // Argument positions of this prototype, for the -i codes.
+    enum { bM = 1, bN, bK, bA, bLda, bStrideA, bB, bLdb, bStrideB, bC, bLdc, bStrideC, bBatch,
+           bTransA, bTransB };
+    const int bad = validate(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, batch != 0);
+    if (bad) {
+        // validate() numbers the arguments as gemm_f32 does; map to this prototype
+        static const int map[] = {0, bM, bN, bK, bA, bLda, bB, bLdb, bC, bLdc, bTransA, bTransB};
+        return -map[-bad];
+    }
+    if (batch < 0 || batch > kDimLimit) return -bBatch;
+    if (strideA < 0) return -bStrideA;
+    if (strideB < 0) return -bStrideB;
+    // Products must not write over each other: C_b spans (M-1)*ldc + N floats.
+    if (strideC < 0 || (batch > 1 && M > 0 && N > 0 && strideC < (M - 1) * ldc + N)) return -bStrideC;
+    if (batch == 0 || M == 0 || N == 0) return 0;
+    Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
+    p.stride_a = strideA;
+    p.stride_b = strideB;
+    p.stride_c = strideC;
+    p.batch = batch;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = K == 0 ? gemmf32::launch_zero_fill(p, s) : gemmf32::launch_mfma(p, s, 0);
+    return err == hipSuccess ? 0 : int(err);
+}
+
+int gemm_f32_version(void) { return 10100; }
 
 }  // extern "C"

@@ -20,6 +20,10 @@ struct Problem {
     float *C;
     int64_t ldc;
     int transA, transB;
+    // Strided batch: product b reads A + b*stride_a, B + b*stride_b and
+    // writes C + b*stride_c, for b < batch (a single product: batch 1).
+    int64_t stride_a = 0, stride_b = 0, stride_c = 0;
+    int64_t batch = 1;
 };
 
 // Each launcher enqueues its kernel(s) on `stream` and returns

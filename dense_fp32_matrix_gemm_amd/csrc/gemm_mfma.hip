@@ -226,8 +226,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::threads, Cfg::threads
                           amdgpu_waves_per_eu(Cfg::wpe, Cfg::wpe))) void
 mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
-            int tiles_m, int tiles_n, int tile_base, int dma_ok)
+            int tiles_m, int tiles_n, int tile_base, int dma_ok, int64_t stride_a,
+            int64_t stride_b, int64_t stride_c, int64_t batch_base)
 {
+    // Strided batch: grid y is the product index.
+    const int64_t bz = batch_base + blockIdx.y;
+    A += bz * stride_a;
+    B += bz * stride_b;
+    C += bz * stride_c;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
     constexpr int FM = Cfg::FM, FN = Cfg::FN;
     using TA = Tile<Cfg, BM, A_KC>;
@@ -465,8 +471,16 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #ifndef GEMM_MFMA_SMALL_CONFIG
 #define GEMM_MFMA_SMALL_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4
 #endif
+#ifndef GEMM_MFMA_KK_CONFIG
+#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 4
+#endif
 using Default = Config<GEMM_MFMA_CONFIG>;
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
+// Large tile when both operands are k-contiguous (A untransposed, B
+// transposed): every DMA row segment is a short run along k, and four
+// 16-k stage buffers in flight hide its latency better (the
+// 8192 x 1024 x 4096 input-gradient product: 125 -> 129 TFLOP/s).
+using DefaultKK = Config<GEMM_MFMA_KK_CONFIG>;
 
 // True if every DMA offset of an operand's stage fits in 32 bits.
 inline bool dma_offsets_fit(int rows, int64_t ld) { return (int64_t(rows) * ld + ld) * 4 < (int64_t(1) << 32); }
@@ -479,14 +493,18 @@ void dispatch(const Problem &p, hipStream_t s)
     const int tiles_m = ceil_div(p.M, Cfg::BM), tiles_n = ceil_div(p.N, Cfg::BN);
     const int64_t tiles = int64_t(tiles_m) * tiles_n;
     const int dma_ok = dma_offsets_fit(TA::rows, p.lda) && dma_offsets_fit(TB::rows, p.ldb);
-    // One workgroup per tile; a grid larger than the cap is split into
-    // launches whose first tile index is a multiple of 8, so the XCD of a
-    // workgroup still follows its tile index.
-    for (int64_t base = 0; base < tiles; base += kMaxGrid) {
-        const int64_t n = tiles - base < kMaxGrid ? tiles - base : kMaxGrid;
-        mfma_kernel<Cfg, A_KC, B_KC, VEC><<<dim3(unsigned(n)), dim3(Cfg::threads), 0, s>>>(
-            p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, int(base),
-            dma_ok);
+    // One workgroup per tile (grid x) and product (grid y); grids larger
+    // than the caps are split into launches whose first tile index is a
+    // multiple of 8, so the XCD of a workgroup still follows its tile index.
+    for (int64_t b0 = 0; b0 < p.batch; b0 += kMaxGridY) {
+        const int64_t nb = p.batch - b0 < kMaxGridY ? p.batch - b0 : kMaxGridY;
+        for (int64_t base = 0; base < tiles; base += kMaxGrid) {
+            const int64_t n = tiles - base < kMaxGrid ? tiles - base : kMaxGrid;
+            mfma_kernel<Cfg, A_KC, B_KC, VEC>
+                <<<dim3(unsigned(n), unsigned(nb)), dim3(Cfg::threads), 0, s>>>(
+                    p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,
+                    int(base), dma_ok, p.stride_a, p.stride_b, p.stride_c, b0);
+        }
     }
 }
 
@@ -499,13 +517,13 @@ void dispatch_vec(const Problem &p, hipStream_t s)
         dispatch<Cfg, A_KC, B_KC, false>(p, s);
 }
 
-template <class Cfg>
+template <class Cfg, class CfgKK = Cfg>
 void dispatch_layout(const Problem &p, hipStream_t s)
 {
     // A is k-contiguous when untransposed; B when transposed.
     const bool a_kc = !p.transA, b_kc = p.transB;
     if (a_kc) {
-        if (b_kc) dispatch_vec<Cfg, true, true>(p, s); else dispatch_vec<Cfg, true, false>(p, s);
+        if (b_kc) dispatch_vec<CfgKK, true, true>(p, s); else dispatch_vec<Cfg, true, false>(p, s);
     } else {
         if (b_kc) dispatch_vec<Cfg, false, true>(p, s); else dispatch_vec<Cfg, false, false>(p, s);
     }
@@ -517,7 +535,8 @@ void dispatch_layout(const Problem &p, hipStream_t s)
 // tile, with each stage's k groups split over two slices of waves, gives
 // more parallelism (measured: S1k 30 -> 88 TFLOP/s, the 2049 x 3071 x 769
 // ragged product 81 -> 86; the 1024 x 4096 x 8192 weight gradient, 256
-// large tiles, stays faster on the large tile).
+// large tiles, stays faster on the large tile).  It is also used when more
+// than a quarter of the large tiles' area would fall outside C (e.g. N = 64).
 #ifndef GEMM_MFMA_SMALL_BELOW
 #define GEMM_MFMA_SMALL_BELOW 256
 #endif
@@ -531,15 +550,18 @@ constexpr int kShortK = 1024;
 hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
 {
     if (tile == 0) {
-        const int64_t big_tiles = int64_t(ceil_div(p.M, Default::BM)) * ceil_div(p.N, Default::BN);
-        const bool small = big_tiles < GEMM_MFMA_SMALL_BELOW ||
+        const int64_t big_tiles =
+            int64_t(ceil_div(p.M, Default::BM)) * ceil_div(p.N, Default::BN) * p.batch;
+        const int64_t area = int64_t(p.M) * p.N * p.batch;
+        const bool wasteful = 4 * area < 3 * big_tiles * Default::BM * Default::BN;
+        const bool small = big_tiles < GEMM_MFMA_SMALL_BELOW || wasteful ||
                            (p.K <= kShortK && big_tiles < GEMM_MFMA_SHORT_K_SMALL_BELOW);
         tile = small ? Small::BM : Default::BM;
     }
     if (tile == Small::BM)
         dispatch_layout<Small>(p, s);
     else
-        dispatch_layout<Default>(p, s);
+        dispatch_layout<Default, DefaultKK>(p, s);
     return hipGetLastError();
 }
 

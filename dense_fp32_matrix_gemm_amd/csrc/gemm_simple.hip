@@ -111,9 +111,12 @@ __global__ __launch_bounds__(T *T) void tiled_kernel(
 }
 
 // ------------------------------------------------------------ zero fill ----
+// C := 0 over M x N of product batch_base + blockIdx.y.
 __global__ __launch_bounds__(256) void zero_fill_kernel(int M, int N, float *__restrict__ C,
-                                                        int64_t ldc)
+                                                        int64_t ldc, int64_t stride_c,
+                                                        int64_t batch_base)
 {
+    C += (batch_base + blockIdx.y) * stride_c;
     const int64_t total = int64_t(M) * N;
     for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < total;
          e += int64_t(gridDim.x) * 256)
@@ -121,6 +124,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(int M, int N, float *__r
 }
 
 constexpr int kMaxGridX = 1 << 20;  // block cap for grid-stride kernels
+constexpr int kMaxGridY = 65535;   // grid y cap (batched fill)
 
 template <int TA, int TB>
 void naive_dispatch(const Problem &p, hipStream_t s)
@@ -165,8 +169,12 @@ hipError_t launch_tiled(const Problem &p, hipStream_t s)
 hipError_t launch_zero_fill(const Problem &p, hipStream_t s)
 {
     const int64_t blocks = (int64_t(p.M) * p.N + 255) / 256;
-    zero_fill_kernel<<<dim3(unsigned(blocks < kMaxGridX ? blocks : kMaxGridX)), dim3(256), 0, s>>>(
-        p.M, p.N, p.C, p.ldc);
+    const unsigned gx = unsigned(blocks < kMaxGridX ? blocks : kMaxGridX);
+    for (int64_t b0 = 0; b0 < p.batch; b0 += kMaxGridY) {
+        const int64_t nb = p.batch - b0 < kMaxGridY ? p.batch - b0 : kMaxGridY;
+        zero_fill_kernel<<<dim3(gx, unsigned(nb)), dim3(256), 0, s>>>(p.M, p.N, p.C, p.ldc,
+                                                                       p.stride_c, b0);
+    }
     return hipGetLastError();
 }
 

@@ -99,6 +99,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = local / gm;
 }
 
-constexpr int kMaxGrid = 1 << 20;  // grid cap; tiled kernels stride over the rest
+constexpr int kMaxGrid = 1 << 20;  // grid x cap; larger grids are split (or strided over)
+constexpr int kMaxGridY = 65535;   // grid y cap (batched products)
 
 }  // namespace gemmf32

@@ -73,6 +73,25 @@ def stored_matrix(seed: int, rows: int, cols: int, ld: Optional[int] = None,
     return out
 
 
+def stored_batch(seed: int, batch: int, rows: int, cols: int, ld: int, gap: int = 0,
+                 dist: str = "u11", pad: float = OPERAND_PAD) -> np.ndarray:
+    """``batch`` stored matrices, each rows x cols with leading dimension ld,
+    laid out one after another with ``gap`` extra floats between them.
+
+    Returns a float32 array of shape (batch, rows * ld + gap): row b is the
+    flat storage of matrix b (stride rows * ld + gap floats); padding and
+    gaps hold ``pad``.
+    """
+    rng = np.random.default_rng(seed)
+    stride = rows * ld + gap
+    out = np.full((batch, stride), pad, dtype=np.float32)
+    if batch and rows and cols:
+        vals = _draw(rng, dist, (batch * rows, cols)).reshape(batch, rows, cols)
+        body = out[:, :rows * ld].reshape(batch, rows, ld)
+        body[:, :, :cols] = vals
+    return out
+
+
 def output_matrix(rows: int, cols: int, ld: Optional[int] = None,
                   fill: float = OUTPUT_PAD) -> np.ndarray:
     """The output buffer: every element (including the padding) set to ``fill``."""
@@ -103,6 +122,9 @@ class Workload:
     ldb: Optional[int] = None
     ldc: Optional[int] = None
     description: str = ""
+    batch: int = 1        # > 1: a strided batch of independent products
+    gap: int = 0          # extra floats between consecutive matrices of a batch
+    shared_b: bool = False  # every product of the batch uses one B (stride 0)
 
     # -- stored shapes -------------------------------------------------
     @property
@@ -125,20 +147,42 @@ class Workload:
     def ldc_(self) -> int:
         return self.ldc if self.ldc is not None else max(1, self.N)
 
+    # Batch strides in floats (0 for a single product or a shared B).
+    @property
+    def stride_a(self) -> int:
+        return self.a_dims[0] * self.lda_ + self.gap if self.batch > 1 else 0
+
+    @property
+    def stride_b(self) -> int:
+        if self.batch == 1 or self.shared_b:
+            return 0
+        return self.b_dims[0] * self.ldb_ + self.gap
+
+    @property
+    def stride_c(self) -> int:
+        return self.M * self.ldc_ + self.gap if self.batch > 1 else 0
+
     @property
     def flops(self) -> int:
-        """2*M*N*K: one multiply and one add per (i, j, k) term."""
-        return 2 * self.M * self.N * self.K
+        """2*M*N*K per product: one multiply and one add per (i, j, k) term."""
+        return 2 * self.M * self.N * self.K * self.batch
 
     def make_a(self) -> np.ndarray:
+        """Single product: (rows, lda).  Batch: (batch, stride_a) flat storage."""
         r, c = self.a_dims
+        if self.batch > 1:
+            return stored_batch(self.seed_a, self.batch, r, c, self.lda_, self.gap, self.dist_a)
         return stored_matrix(self.seed_a, r, c, self.lda_, self.dist_a)
 
     def make_b(self) -> np.ndarray:
         r, c = self.b_dims
+        if self.batch > 1 and not self.shared_b:
+            return stored_batch(self.seed_b, self.batch, r, c, self.ldb_, self.gap, self.dist_b)
         return stored_matrix(self.seed_b, r, c, self.ldb_, self.dist_b)
 
     def make_c(self) -> np.ndarray:
+        if self.batch > 1:
+            return np.full((self.batch, self.stride_c), OUTPUT_PAD, dtype=np.float32)
         return output_matrix(self.M, self.N, self.ldc_)
 
     def make(self) -> Dict[str, np.ndarray]:
@@ -180,6 +224,21 @@ WORKLOADS: Dict[str, Workload] = {
                  description="backward dW = X^T . dY (X stored 8192x1024)"),
     ]
 }
+
+# Batched products of one attention layer over 8 sequences x 8 heads of
+# 512 positions with head size 64: the scores Q . K^T (keys stored position
+# by position, so transposed) and the weighted values P . V.  They stand in
+# for the generation-cache product of the "Rendre le GPU rapide" page.
+BATCHED: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("attn-qk", 512, 512, 64, 3000, 3001, "n01", "n01", transB=1, batch=64,
+                 description="scores Q[64 x 512 x 64] . K^T (K stored 64 x 512 x 64)"),
+        Workload("attn-pv", 512, 64, 512, 3002, 3003, "u11", "n01", batch=64,
+                 description="values P[64 x 512 x 512] . V[64 x 512 x 64]"),
+    ]
+}
+WORKLOADS.update(BATCHED)
 
 # The workload the throughput metric is quoted on.
 HEADLINE = "S4k"

@@ -96,7 +96,25 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 float *C, int64_t ldc,
                 int transA, int transB, void *stream, int algo);
 
-/* A static, human-readable description of a return value (never NULL). */
+/* Strided-batched product: for b = 0 .. batch-1,
+ *     C + b*strideC  =  op(A + b*strideA) . op(B + b*strideB)
+ * with every product as in gemm_f32 (same storage, ld and transpose rules).
+ * This is the attention-score product of the Smallem page ("Rendre le GPU
+ * rapide", section on the generation cache: queries [B,H,N,D] times
+ * transposed keys [B,H,D,T], one product per batch and head).  Strides are
+ * in floats; strideA or strideB 0 shares one operand across the batch;
+ * products must not overlap in C (strideC >= (M-1)*ldc + N when batch > 1).
+ * Return codes as for gemm_f32, with -i numbering THIS prototype's
+ * arguments: -6/-9/-12 a negative or overlapping stride, -13 batch < 0 or
+ * >= 2^31.  batch == 0 returns 0 and writes nothing.  Runs on the MFMA path. */
+int gemm_f32_strided_batched(int64_t M, int64_t N, int64_t K,
+                             const float *A, int64_t lda, int64_t strideA,
+                             const float *B, int64_t ldb, int64_t strideB,
+                             float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                             int transA, int transB, void *stream);
+
+/* A static, human-readable description of a return value (never NULL).
+ * Messages for -i name gemm_f32's arguments. */
 const char *gemm_f32_strerror(int status);
 
 /* Library interface version: major * 10000 + minor * 100 + patch. */

@@ -120,6 +120,31 @@ class Oracle:
         return out
 
 
+def gemm_ref_batched(A: np.ndarray, B: np.ndarray, M: int, N: int, K: int, transA: int,
+                     transB: int, lda: int, stride_a: int, ldb: int, stride_b: int,
+                     batch: int) -> np.ndarray:
+    """The strided-batched product, by definition: for each b, the plain
+    product of the stored matrices starting b*stride floats into the flat
+    buffers A and B.  Returns float64 (batch, M, N).
+
+    Pinned against a single product of block-diagonal matrices
+    (tests/test_oracle_pins.py).
+    """
+    orc = load()
+    A = np.ascontiguousarray(A, dtype=np.float32).reshape(-1)
+    B = np.ascontiguousarray(B, dtype=np.float32).reshape(-1)
+    a_rows = K if transA else M
+    b_rows = N if transB else K
+    out = np.zeros((batch, M, N), dtype=np.float64)
+    for b in range(batch):
+        a = A[b * stride_a: b * stride_a + a_rows * lda].reshape(a_rows, lda) if a_rows else \
+            np.zeros((0, lda), np.float32)
+        bb = B[b * stride_b: b * stride_b + b_rows * ldb].reshape(b_rows, ldb) if b_rows else \
+            np.zeros((0, ldb), np.float32)
+        out[b] = orc.gemm(a, bb, M, N, K, transA, transB)
+    return out
+
+
 def gemm_ref(A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
              transA: int = 0, transB: int = 0) -> np.ndarray:
     """Module-level shorthand for ``load().gemm(...)``."""

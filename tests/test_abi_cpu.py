@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert g.gemm_f32_version() == 10000
+    assert g.gemm_f32_version() == 10100
 
 
 def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
@@ -133,8 +133,39 @@ def test_operand_layout_from_strides():
 def test_header_is_plain_c():
     """The public header compiles as C with no HIP headers on the include path."""
     import subprocess
-    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10000 ? 0 : 1;}\n"
+    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10100 ? 0 : 1;}\n"
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
                        input=src, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def bcall(M=4, N=4, K=4, A=FAKE, lda=None, sA=None, B=FAKE, ldb=None, sB=None, C=FAKE,
+          ldc=None, sC=None, batch=3, ta=0, tb=0):
+    lda = max(1, M if ta else K) if lda is None else lda
+    ldb = max(1, K if tb else N) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    sA = (K if ta else M) * lda if sA is None else sA
+    sB = (N if tb else K) * ldb if sB is None else sB
+    sC = M * ldc if sC is None else sC
+    return g.gemm_f32_strided_batched(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch,
+                                      ta, tb, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(M=-1), -1), (dict(N=-1), -2), (dict(K=-1), -3), (dict(A=None), -4),
+    (dict(lda=3), -5), (dict(sA=-1), -6), (dict(B=None), -7), (dict(ldb=3), -8),
+    (dict(sB=-4), -9), (dict(C=None), -10), (dict(ldc=3), -11), (dict(sC=-1), -12),
+    (dict(sC=15), -12),                     # C products would overlap: 3*4 + 4 = 16 > 15
+    (dict(batch=-1), -13), (dict(batch=BIG), -13), (dict(ta=3), -14), (dict(tb=2), -15),
+])
+def test_strided_batched_invalid_arguments(kwargs, code):
+    assert bcall(**kwargs) == code
+
+
+def test_strided_batched_quick_returns():
+    """batch 0, or an empty product, writes nothing and touches no GPU."""
+    assert bcall(batch=0, A=None, B=None, C=None) == 0
+    assert bcall(M=0, A=None, C=None) == 0
+    assert bcall(sA=0, sB=0, batch=0) == 0          # shared operands are allowed
+    assert bcall(sC=16, batch=0) == 0

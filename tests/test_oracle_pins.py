@@ -99,3 +99,34 @@ def test_nan_propagates(oracle):
     A[1, 2] = np.nan
     C = oracle.gemm(A, B, 3, 5, 4)
     assert np.all(np.isnan(C[1])) and not np.any(np.isnan(C[[0, 2]]))
+
+
+@pytest.mark.parametrize("ta,tb,gap,shared", [(0, 0, 0, False), (1, 0, 3, False),
+                                              (0, 1, 5, True), (1, 1, 1, False)])
+def test_batched_equals_block_diagonal_product(oracle, ta, tb, gap, shared):
+    """A batch of products equals the diagonal blocks of one product of
+    block-diagonal matrices (whose off-diagonal blocks are exactly zero)."""
+    import oracle as oracle_pkg
+    batch, M, N, K = 5, 7, 6, 9
+    w = gi.Workload("bd", M, N, K, 41, 42, transA=ta, transB=tb, batch=batch, gap=gap,
+                    shared_b=shared, lda=(M if ta else K) + 2, ldb=(K if tb else N) + 1)
+    A, B = w.make_a(), w.make_b()
+    got = oracle_pkg.gemm_ref_batched(A, B, M, N, K, ta, tb, w.lda_, w.stride_a, w.ldb_,
+                                      w.stride_b, batch)
+    # logical operands of each product
+    ar, ac = w.a_dims
+    br, bc = w.b_dims
+    a_flat, b_flat = A.reshape(-1), B.reshape(-1)
+    big_a = np.zeros((batch * M, batch * K), np.float32)
+    big_b = np.zeros((batch * K, batch * N), np.float32)
+    for b in range(batch):
+        sa = a_flat[b * w.stride_a: b * w.stride_a + ar * w.lda_].reshape(ar, w.lda_)[:, :ac]
+        sb = b_flat[b * w.stride_b: b * w.stride_b + br * w.ldb_].reshape(br, w.ldb_)[:, :bc]
+        big_a[b * M:(b + 1) * M, b * K:(b + 1) * K] = sa.T if ta else sa
+        big_b[b * K:(b + 1) * K, b * N:(b + 1) * N] = sb.T if tb else sb
+    full = oracle.gemm(big_a, big_b, batch * M, batch * N, batch * K)
+    for b in range(batch):
+        assert np.array_equal(got[b], full[b * M:(b + 1) * M, b * N:(b + 1) * N]), b
+        for c in range(batch):
+            if c != b:
+                assert not np.any(full[b * M:(b + 1) * M, c * N:(c + 1) * N])
