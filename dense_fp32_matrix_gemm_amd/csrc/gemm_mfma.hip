@@ -44,6 +44,7 @@
 //    time, so co-resident workgroups of one XCD share A and B panels in L2.
 #include "tile_common.hpp"
 
+
 namespace gemmf32 {
 namespace {
 
@@ -90,13 +91,16 @@ constexpr int kBlk = 32;  // MFMA output block edge
 // slices are summed through LDS at the end.  It gives small grids more
 // waves per SIMD without any memory outside the output.  NBUF stage
 // buffers let the copy of stage s + NBUF - 1 run while stage s is computed;
-// FOLD stages form one accumulation chunk on that path.
+// FOLD stages form one accumulation chunk on that path.  PREFETCH reads the
+// LDS fragments of the next k group before the current group's MFMAs
+// (faster with one k-slice; slower when two slices already interleave).
 template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int WPE_, int GROUP_M_,
-          int WRITE_G_, int CHAINS_, int KSPLIT_, int NBUF_, int FOLD_>
+          int WRITE_G_, int CHAINS_, int KSPLIT_, int NBUF_, int FOLD_, int PREFETCH_>
 struct Config {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int nbuf = NBUF_;  // LDS stage buffers (copies in flight: NBUF - 1)
     static constexpr int fold = FOLD_;  // stages per accumulation chunk on the copy path
+    static constexpr bool prefetch = PREFETCH_;  // read k group t + 1 before group t's MFMAs
     static constexpr int ksplit = KSPLIT_;                 // k-slices of waves
     static constexpr int waves_mn = WAVES_M * WAVES_N;     // waves per k-slice
     static constexpr int waves = waves_mn * KSPLIT_;
@@ -290,14 +294,24 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         const float *la = lds;
         const float *lb = lds + TA::floats;
         constexpr int kGroups = BK / 8 / Cfg::ksplit;  // k groups per slice per stage
+        // With prefetch, the fragments of k group t + 1 are read before the
+        // MFMAs of group t, so LDS latency overlaps matrix-core work.
+        v4f fa[2][FM], fb[2][FN];
+        auto read = [&](int t, int slot) {
+            const int g = Cfg::ksplit == 1 ? t : t * Cfg::ksplit + kslice;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa[slot][i] = TA::fragment(la, wm + i * kBlk + l32, g, half);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[slot][j] = TB::fragment(lb, wn + j * kBlk + l32, g, half);
+        };
+        if (Cfg::prefetch) read(0, 0);
 #pragma unroll
         for (int t = 0; t < kGroups; ++t) {
-            const int g = Cfg::ksplit == 1 ? t : t * Cfg::ksplit + kslice;
-            v4f fa[FM], fb[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) fa[i] = TA::fragment(la, wm + i * kBlk + l32, g, half);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) fb[j] = TB::fragment(lb, wn + j * kBlk + l32, g, half);
+            const int cur = Cfg::prefetch ? (t & 1) : 0;
+            if (!Cfg::prefetch)
+                read(t, 0);
+            else if (t + 1 < kGroups)
+                read(t + 1, (t + 1) & 1);
             if (Cfg::ksplit == 1 && t == Cfg::write_g) mid();
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -307,7 +321,8 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                     for (int j = 0; j < FN; ++j) {
                         v16f &p = part[u % CH][i][j];
                         p = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            fa[i][u], fb[j][u], (kFresh && t == 0 && u < CH) ? v16f{0.0f} : p, 0, 0, 0);
+                            fa[cur][i][u], fb[cur][j][u],
+                            (kFresh && t == 0 && u < CH) ? v16f{0.0f} : p, 0, 0, 0);
                     }
         }
         if (Cfg::ksplit > 1 || Cfg::write_g >= kGroups) mid();
@@ -466,13 +481,13 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 }
 
 #ifndef GEMM_MFMA_CONFIG
-#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 2
+#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 2, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_CONFIG
-#define GEMM_MFMA_SMALL_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4
+#define GEMM_MFMA_SMALL_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4, 0
 #endif
 #ifndef GEMM_MFMA_KK_CONFIG
-#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 4
+#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 4, 1
 #endif
 using Default = Config<GEMM_MFMA_CONFIG>;
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
