@@ -174,6 +174,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--epilogue", default="none", choices=["none", "bias", "gelu"],
+                    help="time the fused C = act(A.B + bias) entry point instead")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -209,9 +211,20 @@ def main(argv=None) -> int:
     if batched and args.algo not in ("auto", "mfma"):
         print("batched workloads run on the MFMA path only", file=sys.stderr)
         return 2
+    fused = args.epilogue != "none"
+    if fused and (batched or args.algo not in ("auto", "mfma")):
+        print("the fused epilogue runs single products on the MFMA path", file=sys.stderr)
+        return 2
+    bias = gi.stored_matrix(2003, 1, w.N, dist="n002")[0] if fused else None
+    dbias = torch.from_numpy(bias).cuda() if fused else None
+    act = g.ACT_GELU if args.epilogue == "gelu" else g.ACT_NONE
 
     def step(algo=algo_id):
-        if batched:
+        if fused:
+            st = g.gemm_f32_bias_act(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
+                                     dC.data_ptr(), w.ldc_, w.transA, w.transB, dbias.data_ptr(),
+                                     act, stream.cuda_stream)
+        elif batched:
             st = g.gemm_f32_strided_batched(
                 w.M, w.N, w.K, dA.data_ptr(), w.lda_, w.stride_a, dB.data_ptr(), w.ldb_,
                 w.stride_b, dC.data_ptr(), w.ldc_, w.stride_c, w.batch, w.transA, w.transB,
@@ -240,6 +253,9 @@ def main(argv=None) -> int:
             b0 = B if w.shared_b else B[last, :w.b_dims[0] * w.ldb_].reshape(w.b_dims[0], w.ldb_)
             c0 = c0[last, :w.M * w.ldc_].reshape(w.M, w.ldc_)
         ref = oracle.load().entries(a0, b0, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
+        if fused:
+            ref = oracle.load().epilogue((ref + bias[cols].astype(np.float64))[None, :], None,
+                                         act)[0]
         got = c0[rows, cols].astype(np.float64)
         ratio = np.abs(got - ref) / (1e-6 * w.K + 1e-5 * np.abs(ref))
         parity = {"entries": int(rows.size), "max_err_over_bound": float(np.max(ratio)),
@@ -270,6 +286,25 @@ def main(argv=None) -> int:
         tms = _timed(lambda: torch.bmm(ta, tb, out=out), 10, 2)
         context = {"torch.bmm (contiguous copies)": {"tflops": flops / (tms * 1e-3) / 1e12,
                                                      "ms": tms}}
+    elif not args.no_context and fused:
+        ta = dA[:, :w.a_dims[1]]
+        tb = dB[:, :w.b_dims[1]]
+        ta = ta.t() if w.transA else ta
+        tb = tb.t() if w.transB else tb
+        out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+        def unfused():
+            torch.addmm(dbias, ta, tb, out=out)
+            if act == g.ACT_GELU:
+                torch.nn.functional.gelu(out)
+        tms = _timed(unfused, 50, 20)
+        plain = _timed(lambda: g.gemm_f32_ex(
+            w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_, dC.data_ptr(), w.ldc_,
+            w.transA, w.transB, stream.cuda_stream, g.ALGOS["mfma"]), 50, 20)
+        context = {"torch addmm+gelu (unfused)": {"tflops": flops / (tms * 1e-3) / 1e12,
+                                                  "ms": tms},
+                   "gemm_f32 without epilogue": {"tflops": flops / (plain * 1e-3) / 1e12,
+                                                 "ms": plain}}
     elif not args.no_context:
         context = {}
         for other in ("mfma", "fma", "tiled", "naive"):
@@ -314,7 +349,7 @@ def main(argv=None) -> int:
                    "lda": w.lda_,
                    "ldb": w.ldb_, "ldc": w.ldc_, "transA": w.transA, "transB": w.transB,
                    "inputs": w.description, "seeds": [w.seed_a, w.seed_b],
-                   "algo": args.algo, "parallelism": "single GPU"},
+                   "algo": args.algo, "epilogue": args.epilogue, "parallelism": "single GPU"},
         "pct_of_peak": 100.0 * value / MI355X_FP32_PEAK_TFLOPS,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -10,11 +10,12 @@ current stream, and calls the library.  PyTorch owns memory and streams.
 
 from __future__ import annotations
 
-from ._lib import (ALGOS, LibraryNotBuilt, gemm_f32, gemm_f32_ex, gemm_f32_naive,
-                   gemm_f32_strerror, gemm_f32_strided_batched, gemm_f32_version, library_path,
-                   load)
+from ._lib import (ACT_GELU, ACT_NONE, ALGOS, LibraryNotBuilt, gemm_f32, gemm_f32_bias_act,
+                   gemm_f32_ex, gemm_f32_naive, gemm_f32_strerror, gemm_f32_strided_batched,
+                   gemm_f32_version, library_path, load)
 
-__all__ = ["ALGOS", "GemmError", "LibraryNotBuilt", "bmm", "gemm_f32", "gemm_f32_ex",
+__all__ = ["ACT_GELU", "ACT_NONE", "ALGOS", "GemmError", "LibraryNotBuilt", "bmm", "gemm_f32",
+           "gemm_f32_bias_act", "gemm_f32_ex", "linear",
            "gemm_f32_naive", "gemm_f32_strerror", "gemm_f32_strided_batched",
            "gemm_f32_version", "library_path", "load", "matmul", "operand_layout"]
 
@@ -106,6 +107,38 @@ def bmm(a, b, out=None, stream=None):
     st = gemm_f32_strided_batched(M, N, K, a.data_ptr(), lda, a.stride(0), b.data_ptr(), ldb,
                                   b.stride(0), out.data_ptr(), ldc, out.stride(0), batch,
                                   ta, tb, stream)
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def linear(x, w, bias=None, activation=None, out=None, stream=None):
+    """act(x @ w + bias) in one fused call (``activation``: None or "gelu").
+
+    ``x`` is M x K and ``w`` is K x N (either may be a transposed view);
+    ``bias`` is None or a length-N float32 device tensor.
+    """
+    import torch
+
+    if x.dtype != torch.float32 or w.dtype != torch.float32:
+        raise TypeError("linear takes float32 tensors")
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(x.shape)} @ {tuple(w.shape)}")
+    act = {None: ACT_NONE, "gelu": ACT_GELU}[activation]
+    if bias is not None and (bias.shape != (N,) or bias.dtype != torch.float32 or
+                             (N > 1 and bias.stride(0) != 1)):
+        raise ValueError("bias must be a contiguous float32 vector of N entries")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    ta, lda = operand_layout(x)
+    tb, ldb = operand_layout(w)
+    ldc = max(out.stride(0), N, 1) if M > 1 else max(N, 1)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = gemm_f32_bias_act(M, N, K, x.data_ptr(), lda, w.data_ptr(), ldb, out.data_ptr(), ldc,
+                           ta, tb, None if bias is None else bias.data_ptr(), act, stream)
     if st != 0:
         raise GemmError(st)
     return out

@@ -27,6 +27,8 @@ SIGNATURES = {
     "gemm_f32_ex": (_int, _GEMM_ARGS + [_int]),
     "gemm_f32_strided_batched": (_int, [_i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64,
                                         _ptr, _i64, _i64, _i64, _int, _int, _ptr]),
+    "gemm_f32_bias_act": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
+                                 _ptr, _int, _ptr]),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
     "gemm_f32_version": (_int, []),
 }
@@ -83,6 +85,14 @@ def gemm_f32_strided_batched(M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, 
                              batch, transA, transB, stream) -> int:
     return _call("gemm_f32_strided_batched", M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc,
                  strideC, batch, transA, transB, stream)
+
+
+ACT_NONE, ACT_GELU = 0, 1
+
+
+def gemm_f32_bias_act(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, bias, act, stream) -> int:
+    return _call("gemm_f32_bias_act", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, bias, act,
+                 stream)
 
 
 def gemm_f32_strerror(status: int) -> str:

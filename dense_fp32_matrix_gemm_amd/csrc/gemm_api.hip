@@ -150,6 +150,26 @@ int gemm_f32_strided_batched(int64_t M, int64_t N, int64_t K, const float *A, in
     return err == hipSuccess ? 0 : int(err);
 }
 
-int gemm_f32_version(void) { return 10100; }
+int gemm_f32_bias_act(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                      const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
+                      int transB, const float *bias, int act, void *stream)
+{
+    const int bad = validate(M, N, K, A, lda, B, ldb, C, ldc, transA, transB);
+    if (bad) return bad;
+    if (act != GEMM_F32_ACT_NONE && act != GEMM_F32_ACT_GELU) return -13;
+    if (M == 0 || N == 0) return 0;
+    Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
+    p.bias = bias;
+    p.act = act;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (K == 0)  // the empty product is 0: C = act(bias) (or act(0))
+        err = gemmf32::launch_zero_fill(p, s);
+    else
+        err = gemmf32::launch_mfma(p, s, 0);
+    return err == hipSuccess ? 0 : int(err);
+}
+
+int gemm_f32_version(void) { return 10200; }
 
 }  // extern "C"

@@ -24,6 +24,9 @@ struct Problem {
     // writes C + b*stride_c, for b < batch (a single product: batch 1).
     int64_t stride_a = 0, stride_b = 0, stride_c = 0;
     int64_t batch = 1;
+    // Fused epilogue: C = act(product + bias[j]); bias may be null.
+    const float *bias = nullptr;
+    int act = 0;  // 0: none, 1: GELU (erf form)
 };
 
 // Each launcher enqueues its kernel(s) on `stream` and returns
@@ -33,8 +36,16 @@ hipError_t launch_tiled(const Problem &p, hipStream_t stream);
 hipError_t launch_fma(const Problem &p, hipStream_t stream);
 // tile: 0 chooses by problem size; 128 or 64 forces that tile edge.
 hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
-// C := 0 over M x N (the empty sum, K == 0).  Assumes M, N >= 1.
+// C := act(0 + bias[j]) over M x N (the empty sum, K == 0), for every
+// product of the batch.  Assumes M, N >= 1.
 hipError_t launch_zero_fill(const Problem &p, hipStream_t stream);
+
+// GELU in its exact form x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), Phi the
+// standard normal distribution function.
+__device__ __forceinline__ float gelu(float x)
+{
+    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+}
 
 // Number of 32-bit words per 16-byte vector.
 constexpr int kVec = 4;

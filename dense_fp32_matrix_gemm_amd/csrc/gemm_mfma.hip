@@ -231,7 +231,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::threads, Cfg::threads
 mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
             int tiles_m, int tiles_n, int tile_base, int dma_ok, int64_t stride_a,
-            int64_t stride_b, int64_t stride_c, int64_t batch_base)
+            int64_t stride_b, int64_t stride_c, int64_t batch_base,
+            const float *__restrict__ bias, int act)
 {
     // Strided batch: grid y is the product index.
     const int64_t bz = batch_base + blockIdx.y;
@@ -466,16 +467,21 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     }
 
     // Epilogue.  Lane l of a 32 x 32 block holds column l % 32 and, in
-    // accumulator slot v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.
+    // accumulator slot v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.  The fused
+    // variant adds bias[column] and applies the activation before the store
+    // (both flags are uniform over the launch).
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col = n0 + wn + j * kBlk + l32;
+            const float bj = (bias != nullptr && col < N) ? bias[col] : 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = m0 + wm + i * kBlk + 8 * (v / 4) + 4 * half + (v % 4);
-                if (inside || (row < M && col < N)) C[int64_t(row) * ldc + col] = acc[i][j][v];
+                float x = acc[i][j][v] + bj;
+                if (act == 1) x = gelu(x);
+                if (inside || (row < M && col < N)) C[int64_t(row) * ldc + col] = x;
             }
         }
 }
@@ -518,7 +524,7 @@ void dispatch(const Problem &p, hipStream_t s)
             mfma_kernel<Cfg, A_KC, B_KC, VEC>
                 <<<dim3(unsigned(n), unsigned(nb)), dim3(Cfg::threads), 0, s>>>(
                     p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,
-                    int(base), dma_ok, p.stride_a, p.stride_b, p.stride_c, b0);
+                    int(base), dma_ok, p.stride_a, p.stride_b, p.stride_c, b0, p.bias, p.act);
         }
     }
 }

@@ -111,16 +111,22 @@ __global__ __launch_bounds__(T *T) void tiled_kernel(
 }
 
 // ------------------------------------------------------------ zero fill ----
-// C := 0 over M x N of product batch_base + blockIdx.y.
+// C := act(0 + bias[j]) over M x N of product batch_base + blockIdx.y
+// (without bias and activation: zero).
 __global__ __launch_bounds__(256) void zero_fill_kernel(int M, int N, float *__restrict__ C,
                                                         int64_t ldc, int64_t stride_c,
-                                                        int64_t batch_base)
+                                                        int64_t batch_base,
+                                                        const float *__restrict__ bias, int act)
 {
     C += (batch_base + blockIdx.y) * stride_c;
     const int64_t total = int64_t(M) * N;
     for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < total;
-         e += int64_t(gridDim.x) * 256)
-        C[(e / N) * ldc + e % N] = 0.0f;
+         e += int64_t(gridDim.x) * 256) {
+        const int64_t j = e % N;
+        float x = bias != nullptr ? bias[j] : 0.0f;
+        if (act == 1) x = gelu(x);
+        C[(e / N) * ldc + j] = x;
+    }
 }
 
 constexpr int kMaxGridX = 1 << 20;  // block cap for grid-stride kernels
@@ -173,7 +179,8 @@ hipError_t launch_zero_fill(const Problem &p, hipStream_t s)
     for (int64_t b0 = 0; b0 < p.batch; b0 += kMaxGridY) {
         const int64_t nb = p.batch - b0 < kMaxGridY ? p.batch - b0 : kMaxGridY;
         zero_fill_kernel<<<dim3(gx, unsigned(nb)), dim3(256), 0, s>>>(p.M, p.N, p.C, p.ldc,
-                                                                       p.stride_c, b0);
+                                                                       p.stride_c, b0, p.bias,
+                                                                       p.act);
     }
     return hipGetLastError();
 }

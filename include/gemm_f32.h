@@ -113,6 +113,28 @@ int gemm_f32_strided_batched(int64_t M, int64_t N, int64_t K,
                              float *C, int64_t ldc, int64_t strideC, int64_t batch,
                              int transA, int transB, void *stream);
 
+/* Epilogues of gemm_f32_bias_act. */
+enum gemm_f32_act {
+    GEMM_F32_ACT_NONE = 0,
+    GEMM_F32_ACT_GELU = 1  /* x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)) */
+};
+
+/* Fused linear layer: C = act(op(A) . op(B) + bias), the bias added to every
+ * row (bias[j] for column j; bias may be NULL for none), the activation
+ * applied elementwise in FP32 before C is written.  The Smallem page
+ * ("Rendre le GPU rapide", sections on fused kernels and on the comparison
+ * with PyTorch) gives GELU its own kernel and names the unfused bias add as
+ * a cost; here both ride in the product's store.  bias, if not NULL, is a
+ * device array of N floats.  Storage, ownership and the other codes as for
+ * gemm_f32; -13: act not a gemm_f32_act value.  K == 0 writes act(bias).
+ * Runs on the MFMA path. */
+int gemm_f32_bias_act(int64_t M, int64_t N, int64_t K,
+                      const float *A, int64_t lda,
+                      const float *B, int64_t ldb,
+                      float *C, int64_t ldc,
+                      int transA, int transB,
+                      const float *bias, int act, void *stream);
+
 /* A static, human-readable description of a return value (never NULL).
  * Messages for -i name gemm_f32's arguments. */
 const char *gemm_f32_strerror(int status);

@@ -64,6 +64,8 @@ class Oracle:
         lib.gemm_ref_f64_entries.argtypes = [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64,
                                              ctypes.c_int, ctypes.c_int, _i64,
                                              _ptr, _ptr, _ptr]
+        lib.gemm_ref_epilogue.restype = ctypes.c_int
+        lib.gemm_ref_epilogue.argtypes = [_i64, _i64, _ptr, _i64, _ptr, ctypes.c_int]
         lib.gemm_ref_threads.restype = ctypes.c_int
         lib.gemm_ref_threads.argtypes = []
         self._lib = lib
@@ -96,6 +98,23 @@ class Oracle:
         if with_stats:
             return C, (int(stats[0]), int(stats[1]))
         return C
+
+    def epilogue(self, C: np.ndarray, bias: Optional[np.ndarray] = None, act: int = 0) -> np.ndarray:
+        """act(C + bias) in float64 (a new array); C is (M, N) float64, bias N float32.
+
+        act 0: identity; act 1: GELU, x * Phi(x).  Pinned: normal-distribution
+        values, gelu(x) - gelu(-x) = x, limits, scipy's erf.
+        """
+        out = np.ascontiguousarray(C, dtype=np.float64).copy()
+        M, N = out.shape
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        if b is not None and b.shape != (N,):
+            raise ValueError("bias has N entries")
+        rc = self._lib.gemm_ref_epilogue(M, N, out.ctypes.data, max(N, 1),
+                                         None if b is None else b.ctypes.data, int(act))
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (status {rc})")
+        return out
 
     def entries(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
                 transA: int, transB: int, rows: np.ndarray,

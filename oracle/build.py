@@ -21,7 +21,7 @@ CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra"]
 def build(source: str = SOURCE, output: str = LIBRARY, verbose: bool = False) -> str:
     """Compile ``source`` into the shared library ``output`` and return its path."""
     tmp = output + ".tmp"
-    cmd = ["gcc", *CFLAGS, source, "-o", tmp]
+    cmd = ["gcc", *CFLAGS, source, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -35,6 +35,7 @@
  * (one from A and one from B per multiply-add), which is how section 3.1 of
  * the course page counts the naive kernel's operations and bytes.
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -110,6 +111,27 @@ int gemm_ref_f64_entries(int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t t = 0; t < count; ++t)
         out[t] = dot(K, A, lda, transA, B, ldb, transB, rows[t], cols[t]);
+    return 0;
+}
+
+/*
+ * Fused-epilogue reference, in place on a double result:
+ *     C[i][j] = act(C[i][j] + bias[j])      (bias may be NULL: no bias)
+ * act 0: identity.  act 1: GELU, x * Phi(x) with Phi the standard normal
+ * distribution function, Phi(x) = (1 + erf(x / sqrt 2)) / 2.  Both in double.
+ * Returns 0, or -1 for an unknown act.
+ */
+int gemm_ref_epilogue(int64_t M, int64_t N, double *C, int64_t ldc,
+                      const float *bias, int act)
+{
+    if (act != 0 && act != 1) return -1;
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double x = C[i * ldc + j] + (bias ? (double)bias[j] : 0.0);
+            if (act == 1) x = x * 0.5 * (1.0 + erf(x / sqrt(2.0)));
+            C[i * ldc + j] = x;
+        }
+    }
     return 0;
 }
 

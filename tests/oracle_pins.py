@@ -163,3 +163,38 @@ def pin_counts(gemm_with_stats: Callable) -> None:
 
 
 ALL_FAST_PINS = (pin_identity, pin_all_ones, pin_rank_one, pin_integer_exact)
+
+
+# Standard normal distribution function Phi at a few points (statistics-table
+# values); GELU(x) = x * Phi(x).
+PHI_TABLE = {1.0: 0.8413447460685429, 2.0: 0.9772498680518208, -1.5: 0.06680720126885807,
+             0.5: 0.6914624612740131, -3.0: 0.0013498980316301035}
+
+
+def pin_epilogue(epilogue) -> None:
+    """The fused-epilogue reference against closed forms and a library erf.
+
+    ``epilogue(C, bias, act)`` returns act(C + bias) in float64.
+    """
+    import math
+    from scipy.special import erf
+    x = np.array([list(PHI_TABLE)], dtype=np.float64)
+    got = epilogue(x, None, 1)[0]
+    for k, (xv, phi) in enumerate(PHI_TABLE.items()):
+        assert abs(got[k] - xv * phi) <= 1e-15 * max(1.0, abs(xv)), (xv, got[k])
+    rng = np.random.default_rng(106)
+    v = rng.normal(0, 3, size=(40, 50))
+    g_pos, g_neg = epilogue(v, None, 1), epilogue(-v, None, 1)
+    assert np.all(np.abs((g_pos - g_neg) - v) <= 1e-14 * np.maximum(1, np.abs(v)))  # x Phi(x) + x Phi(-x) = x
+    ref = 0.5 * v * (1 + erf(v / math.sqrt(2)))
+    assert np.all(np.abs(g_pos - ref) <= 1e-15 * np.maximum(1, np.abs(v)))
+    big = np.array([[10.0, -10.0, 0.0]])
+    gb = epilogue(big, None, 1)[0]
+    assert abs(gb[0] - 10.0) < 1e-15 and abs(gb[1]) < 1e-20 and gb[2] == 0.0
+    bias = rng.uniform(-1, 1, size=50).astype(np.float32)
+    assert np.array_equal(epilogue(v, bias, 0), v + bias.astype(np.float64)[None, :])
+    assert np.array_equal(epilogue(v, None, 0), v)
+    both = epilogue(v, bias, 1)
+    vb = v + bias.astype(np.float64)[None, :]
+    assert np.all(np.abs(both - 0.5 * vb * (1 + erf(vb / math.sqrt(2)))) <=
+                  1e-15 * np.maximum(1, np.abs(vb)))

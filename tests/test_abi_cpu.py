@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert g.gemm_f32_version() == 10100
+    assert g.gemm_f32_version() == 10200
 
 
 def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
@@ -133,7 +133,7 @@ def test_operand_layout_from_strides():
 def test_header_is_plain_c():
     """The public header compiles as C with no HIP headers on the include path."""
     import subprocess
-    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10100 ? 0 : 1;}\n"
+    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10200 ? 0 : 1;}\n"
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
                        input=src, capture_output=True, text=True)
@@ -169,3 +169,22 @@ def test_strided_batched_quick_returns():
     assert bcall(M=0, A=None, C=None) == 0
     assert bcall(sA=0, sB=0, batch=0) == 0          # shared operands are allowed
     assert bcall(sC=16, batch=0) == 0
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(M=-1), -1), (dict(A=None), -4), (dict(lda=3), -5), (dict(C=None), -8),
+    (dict(ta=2), -10), (dict(act=2), -13), (dict(act=-1), -13),
+])
+def test_bias_act_invalid_arguments(kwargs, code):
+    act = kwargs.pop("act", 1)
+    M, K = kwargs.get("M", 4), 4
+    args = dict(M=M, N=4, K=K, A=FAKE, lda=4, B=FAKE, ldb=4, C=FAKE, ldc=4, ta=0, tb=0)
+    args.update(kwargs)
+    st = g.gemm_f32_bias_act(args["M"], args["N"], args["K"], args["A"], args["lda"], args["B"],
+                             args["ldb"], args["C"], args["ldc"], args["ta"], args["tb"], None,
+                             act, None)
+    assert st == code
+
+
+def test_bias_act_quick_return():
+    assert g.gemm_f32_bias_act(0, 4, 4, None, 4, FAKE, 4, None, 4, 0, 0, None, 1, None) == 0

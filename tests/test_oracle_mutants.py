@@ -40,6 +40,8 @@ MUTANTS = {
                           "C[j * ldc + i] = dot(K, A, lda, transA, B, ldb, transB, i, j);"),
     "miscounted_macs": ("macs += K;", "macs += K - (K > 1);"),
     "miscounted_reads": ("reads += 2 * K;", "reads += K;"),
+    "gelu_wrong_scale": ("erf(x / sqrt(2.0))", "erf(x / 2.0)"),
+    "bias_by_row": ("(bias ? (double)bias[j] : 0.0)", "(bias ? (double)bias[i % N] : 0.0)"),
 }
 
 
@@ -55,6 +57,7 @@ def _all_pins(orc):
     yield "numpy_S1k", lambda: pins.pin_numpy_f64(gemm, gi.WORKLOADS["S1k"])
     yield "counts", lambda: pins.pin_counts(
         lambda A, B, M, N, K: orc.gemm(A, B, M, N, K, 0, 0, with_stats=True))
+    yield "epilogue", lambda: pins.pin_epilogue(orc.epilogue)
 
 
 def _caught(orc):

@@ -130,3 +130,7 @@ def test_batched_equals_block_diagonal_product(oracle, ta, tb, gap, shared):
         for c in range(batch):
             if c != b:
                 assert not np.any(full[b * M:(b + 1) * M, c * N:(c + 1) * N])
+
+
+def test_epilogue(oracle):
+    pins.pin_epilogue(oracle.epilogue)
