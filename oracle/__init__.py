@@ -66,6 +66,13 @@ class Oracle:
                                              _ptr, _ptr, _ptr]
         lib.gemm_ref_epilogue.restype = ctypes.c_int
         lib.gemm_ref_epilogue.argtypes = [_i64, _i64, _ptr, _i64, _ptr, ctypes.c_int]
+        lib.gemm_ref_f64_bf16.restype = ctypes.c_int
+        lib.gemm_ref_f64_bf16.argtypes = [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64,
+                                          _ptr, _i64, ctypes.c_int, ctypes.c_int]
+        lib.gemm_ref_f64_bf16_entries.restype = ctypes.c_int
+        lib.gemm_ref_f64_bf16_entries.argtypes = lib.gemm_ref_f64_entries.argtypes
+        lib.gemm_ref_round_bf16.restype = None
+        lib.gemm_ref_round_bf16.argtypes = [_i64, _ptr, _ptr]
         lib.gemm_ref_threads.restype = ctypes.c_int
         lib.gemm_ref_threads.argtypes = []
         self._lib = lib
@@ -98,6 +105,51 @@ class Oracle:
         if with_stats:
             return C, (int(stats[0]), int(stats[1]))
         return C
+
+    def round_bf16(self, x: np.ndarray) -> np.ndarray:
+        """Each float32 element rounded to the nearest bf16 (ties to even),
+        returned as float32.  Pinned: hand-worked ties and carries, an exact
+        rational rounding, torch's CPU bfloat16 conversion."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty_like(x)
+        self._lib.gemm_ref_round_bf16(x.size, x.ctypes.data, out.ctypes.data)
+        return out
+
+    def gemm_bf16(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+                  transA: int = 0, transB: int = 0) -> np.ndarray:
+        """Mixed precision: sum_k bf16(opA(i,k)) * bf16(opB(k,j)) in float64, (M, N).
+
+        Pinned: small-integer exactness, identity, brute force against exact
+        rationals of independently rounded operands, numpy float64 matmul of
+        torch-rounded operands.
+        """
+        A = _as_stored(A)
+        B = _as_stored(B)
+        C = np.zeros((M, max(N, 1)), dtype=np.float64)
+        rc = self._lib.gemm_ref_f64_bf16(M, N, K, A.ctypes.data, A.shape[1], B.ctypes.data,
+                                         B.shape[1], C.ctypes.data, C.shape[1], int(transA),
+                                         int(transB))
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (status {rc})")
+        return C[:, :N]
+
+    def entries_bf16(self, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+                     transA: int, transB: int, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+        """Selected entries of ``gemm_bf16``.  Pinned against ``gemm_bf16``."""
+        A = _as_stored(A)
+        B = _as_stored(B)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        if rows.shape != cols.shape:
+            raise ValueError("rows and cols differ in length")
+        out = np.empty(rows.shape, dtype=np.float64)
+        rc = self._lib.gemm_ref_f64_bf16_entries(M, N, K, A.ctypes.data, A.shape[1],
+                                                 B.ctypes.data, B.shape[1], int(transA),
+                                                 int(transB), rows.size, rows.ctypes.data,
+                                                 cols.ctypes.data, out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle rejected arguments (status {rc})")
+        return out
 
     def epilogue(self, C: np.ndarray, bias: Optional[np.ndarray] = None, act: int = 0) -> np.ndarray:
         """act(C + bias) in float64 (a new array); C is (M, N) float64, bias N float32.

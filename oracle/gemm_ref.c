@@ -38,6 +38,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 static double op_a(const float *A, int64_t lda, int transA, int64_t i, int64_t k)
 {
@@ -132,6 +133,82 @@ int gemm_ref_epilogue(int64_t M, int64_t N, double *C, int64_t ldc,
             C[i * ldc + j] = x;
         }
     }
+    return 0;
+}
+
+/*
+ * Mixed precision (the Smallem page, "Rendre le GPU rapide", section "Les
+ * Tensor Cores").  A bf16 is the upper 16 bits of a float32: same sign and
+ * exponent, 7 stored significand bits.  The page rounds to the nearest bf16
+ * by adding half a step to the 32-bit pattern before dropping its low 16
+ * bits; the half step is 0x7FFF plus the lowest bit that is kept, so an
+ * exact tie goes to the neighbour whose last kept bit is 0 (ties to even).
+ * The carry out of the significand moves the exponent up, and the largest
+ * values round to infinity, as the bit pattern arithmetic gives by itself.
+ * NaN is returned unchanged (the page does not treat it).  The result is
+ * returned as the float32 it stands for (low 16 bits zero).
+ */
+static float round_bf16(float x)
+{
+    if (isnan(x)) return x;
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    u &= 0xFFFF0000u;
+    memcpy(&x, &u, sizeof x);
+    return x;
+}
+
+/* out[t] = round_bf16(in[t]) for t < n. */
+void gemm_ref_round_bf16(int64_t n, const float *in, float *out)
+{
+    for (int64_t t = 0; t < n; ++t) out[t] = round_bf16(in[t]);
+}
+
+/* One element of the mixed-precision product: each operand element rounded
+ * to bf16, the exact product of the two rounded values summed in double,
+ * k in increasing order.  (A product of two bf16 values has at most 16
+ * significant bits, so it is exact in double.) */
+static double dot_bf16(int64_t K, const float *A, int64_t lda, int transA,
+                       const float *B, int64_t ldb, int transB, int64_t i, int64_t j)
+{
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        const float a = round_bf16((float)op_a(A, lda, transA, i, k));
+        const float b = round_bf16((float)op_b(B, ldb, transB, k, j));
+        s += (double)a * (double)b;
+    }
+    return s;
+}
+
+/*
+ * Mixed-precision product: C[i][j] = sum_k bf16(opA(i,k)) * bf16(opB(k,j)),
+ * in double, storage as gemm_ref_f64.  Returns 0, or -1 on bad arguments.
+ */
+int gemm_ref_f64_bf16(int64_t M, int64_t N, int64_t K,
+                      const float *A, int64_t lda, const float *B, int64_t ldb,
+                      double *C, int64_t ldc, int transA, int transB)
+{
+    if (!args_ok(M, N, K, lda, ldb, transA, transB) || ldc < N) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            C[i * ldc + j] = dot_bf16(K, A, lda, transA, B, ldb, transB, i, j);
+    return 0;
+}
+
+/* Selected entries of the mixed-precision product, as gemm_ref_f64_entries. */
+int gemm_ref_f64_bf16_entries(int64_t M, int64_t N, int64_t K,
+                              const float *A, int64_t lda, const float *B, int64_t ldb,
+                              int transA, int transB, int64_t count,
+                              const int64_t *rows, const int64_t *cols, double *out)
+{
+    if (!args_ok(M, N, K, lda, ldb, transA, transB) || count < 0) return -1;
+    for (int64_t t = 0; t < count; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return -2;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < count; ++t)
+        out[t] = dot_bf16(K, A, lda, transA, B, ldb, transB, rows[t], cols[t]);
     return 0;
 }
 

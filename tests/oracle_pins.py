@@ -198,3 +198,163 @@ def pin_epilogue(epilogue) -> None:
     vb = v + bias.astype(np.float64)[None, :]
     assert np.all(np.abs(both - 0.5 * vb * (1 + erf(vb / math.sqrt(2)))) <=
                   1e-15 * np.maximum(1, np.abs(vb)))
+
+
+# ---------------------------------------------------------------------------
+# Mixed precision (the Smallem page, "Rendre le GPU rapide", section "Les
+# Tensor Cores"): operands rounded to bf16, to nearest with ties to even.
+
+def bf16_nearest(x: float) -> float:
+    """The bf16 nearest to ``x`` (ties to even), by exact rational arithmetic.
+
+    Written from the format, not from bit patterns: bf16 keeps 8 significant
+    bits and the exponent range of float32, so in the binade [2^(e-1), 2^e)
+    its values are the multiples of 2^(e-8), and below 2^-126 the multiples
+    of 2^-133 (its subnormals).  A value that rounds to 2^128 overflows to
+    infinity.  Zeros keep their sign.
+    """
+    import math
+    if x == 0 or math.isinf(x) or math.isnan(x):
+        return x
+    _, e = math.frexp(abs(x))                  # |x| in [2^(e-1), 2^e)
+    quantum = Fraction(2) ** max(e - 8, -133)
+    t = Fraction(abs(x)) / quantum
+    n = math.floor(t)
+    rest = t - n
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = n * quantum
+    if v >= Fraction(2) ** 128:
+        return math.copysign(math.inf, x)
+    return math.copysign(float(v), x)
+
+
+def _f32_from_bits(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint32).view(np.float32)
+
+
+def _finite_patterns(rng, n: int) -> np.ndarray:
+    x = _f32_from_bits(rng.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32))
+    return x[np.isfinite(x)]
+
+
+# (input, nearest bf16) worked by hand from the format: 1 + 2^-8 lies halfway
+# between 1 and 1 + 2^-7; 2^-134 halfway between 0 and the least subnormal
+# 2^-133; 255 * 2^120 is the largest finite bf16 and 2^128 - 2^119 the tie
+# above it; 257 and 259 are ties between multiples of 2 (quantum in [256, 512));
+# float32(0.1) = 0x3DCCCCCD, whose upper half rounds up to 0x3DCD.
+BF16_CASES = [
+    (1.0, 1.0), (1 + 2.0 ** -7, 1 + 2.0 ** -7), (1 + 2.0 ** -8, 1.0),
+    (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6), (1 + 2.0 ** -8 + 2.0 ** -23, 1 + 2.0 ** -7),
+    (1 + 2.0 ** -9, 1.0), (-(1 + 2.0 ** -8), -1.0), (-(1 + 3 * 2.0 ** -8), -(1 + 2.0 ** -6)),
+    (2 - 2.0 ** -9, 2.0), (257.0, 256.0), (259.0, 260.0), (float(np.float32(0.1)), 0.10009765625),
+    (255 * 2.0 ** 120, 255 * 2.0 ** 120), (2.0 ** 128 - 2.0 ** 119, float("inf")),
+    (2.0 ** 128 - 2.0 ** 120 + 2.0 ** 118, 255 * 2.0 ** 120),
+    (float(np.finfo(np.float32).max), float("inf")),
+    (2.0 ** -133, 2.0 ** -133), (2.0 ** -134, 0.0), (3 * 2.0 ** -135, 2.0 ** -133),
+    (2.0 ** -149, 0.0), (2.0 ** -126, 2.0 ** -126), (float("inf"), float("inf")),
+    (float("-inf"), float("-inf")),
+] + [(float(v), float(v)) for v in range(-8, 9)]
+
+
+def pin_bf16_rounding(round_bf16) -> None:
+    """``round_bf16(float32 array) -> float32 array`` against hand-worked
+    cases, the exact rational rounding above, and torch's CPU conversion."""
+    import math
+
+    import torch
+    x = np.array([c[0] for c in BF16_CASES], dtype=np.float32)
+    want = np.array([c[1] for c in BF16_CASES], dtype=np.float32)
+    assert np.array_equal(x.astype(np.float64), [c[0] for c in BF16_CASES]), "cases are float32"
+    got = round_bf16(x)
+    for xi, g, w in zip(x, got, want):
+        assert g == w, (float(xi), float(g), float(w))
+    z = round_bf16(np.array([0.0, -0.0, np.nan], dtype=np.float32))
+    assert z[0] == 0 and not math.copysign(1, z[0]) < 0
+    assert z[1] == 0 and math.copysign(1, z[1]) < 0
+    assert np.isnan(z[2])
+
+    rng = np.random.default_rng(107)
+    sample = _finite_patterns(rng, 6000)
+    ties = _f32_from_bits((rng.integers(0, 2 ** 16, size=3000).astype(np.uint32) << 16) | 0x8000)
+    ties = ties[np.isfinite(ties)]
+    for v in np.concatenate([sample, ties]):
+        g = float(round_bf16(np.array([v], dtype=np.float32))[0])
+        w = bf16_nearest(float(v))
+        assert g == w or (math.isnan(g) and math.isnan(w)), (float(v), g, w)
+        assert math.copysign(1, g) == math.copysign(1, w), float(v)
+
+    many = np.concatenate([_finite_patterns(rng, 400000), ties,
+                           rng.normal(0, 1, 200000).astype(np.float32)])
+    ref = torch.from_numpy(many).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(round_bf16(many).view(np.uint32), ref.view(np.uint32))
+
+
+def _bf16_logical(stored: np.ndarray, dims, trans: int) -> np.ndarray:
+    """Logical operand with each element rounded by torch's CPU bfloat16
+    conversion (a library rounding, independent of the oracle), float64."""
+    import torch
+    m = _logical(stored, dims, trans).astype(np.float32)
+    return torch.from_numpy(np.ascontiguousarray(m)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def pin_bf16_gemm(gemm_bf16) -> None:
+    """The mixed-precision product ``gemm_bf16(A, B, M, N, K, transA, transB)``.
+
+    * Integers in [-8, 8] are bf16 values and their products' sums are
+      exact: the result is the exact integer product (the page's own test
+      for the matrix-core kernel).
+    * Times the identity it returns the rounded operand itself.
+    * On tiny shapes, the exact rational sum of the products of the
+      independently rounded operands, within the double sum's rounding.
+    * On a 64 x 64 x 64 workload, numpy's float64 matmul of the torch-rounded
+      operands, within twice the double sums' error bound.
+    """
+    rng = np.random.default_rng(108)
+    for (M, N, K) in [(9, 13, 31), (64, 48, 200)]:
+        a = rng.integers(-8, 9, size=(M, K))
+        b = rng.integers(-8, 9, size=(K, N))
+        exact = (a @ b).astype(np.float64)
+        for ta, tb in LAYOUTS:
+            C = gemm_bf16(_store(a.astype(np.float32), ta, 2), _store(b.astype(np.float32), tb, 1),
+                          M, N, K, ta, tb)
+            assert np.array_equal(C, exact), ("int", M, N, K, ta, tb)
+
+    nearest = np.vectorize(bf16_nearest, otypes=[np.float64])
+    for (M, K) in [(5, 7), (33, 9)]:
+        a = _rand(rng, (M, K))
+        for ta, tb in LAYOUTS:
+            C = gemm_bf16(_store(a, ta, 1), _store(np.eye(K, dtype=np.float32), tb, 0),
+                          M, K, K, ta, tb)
+            assert np.array_equal(C, nearest(a.astype(np.float64))), ("A.I", M, K, ta, tb)
+            C = gemm_bf16(_store(np.eye(M, dtype=np.float32), ta, 0), _store(a, tb, 2),
+                          M, K, M, ta, tb)
+            assert np.array_equal(C, nearest(a.astype(np.float64))), ("I.B", M, K, ta, tb)
+
+    u = 2.0 ** -53
+    for M in range(1, 4):
+        for N in range(1, 4):
+            for K in range(1, 5):
+                a = _rand(rng, (M, K))
+                b = _rand(rng, (K, N))
+                ra = [[Fraction(bf16_nearest(float(a[i, k]))) for k in range(K)] for i in range(M)]
+                rb = [[Fraction(bf16_nearest(float(b[k, j]))) for j in range(N)] for k in range(K)]
+                for ta, tb in LAYOUTS:
+                    C = gemm_bf16(_store(a, ta, 1), _store(b, tb, 0), M, N, K, ta, tb)
+                    for i in range(M):
+                        for j in range(N):
+                            terms = [ra[i][k] * rb[k][j] for k in range(K)]
+                            exact = sum(terms, Fraction(0))
+                            bound = (K - 1) * u * float(sum(abs(t) for t in terms))
+                            assert abs(Fraction(float(C[i, j])) - exact) <= Fraction(bound), \
+                                (M, N, K, ta, tb, i, j)
+
+    w = gi.WORKLOADS["S64"]
+    for ta, tb in LAYOUTS:
+        wl = gi.make_case(w.M, w.N, w.K, ta, tb, 1, "u11", seed=109 + 2 * ta + tb)
+        A, B = wl.make_a(), wl.make_b()
+        C = gemm_bf16(A, B, wl.M, wl.N, wl.K, ta, tb)
+        a = _bf16_logical(A, wl.a_dims, ta)
+        b = _bf16_logical(B, wl.b_dims, tb)
+        bound = 2 * wl.K * u * (np.abs(a) @ np.abs(b))
+        assert np.all(np.abs(C - a @ b) <= bound), ("numpy", ta, tb)

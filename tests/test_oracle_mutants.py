@@ -2,7 +2,7 @@
 
 Each mutant is the oracle's C source with one textual change (a dropped
 term, a flipped sign, a swapped index, a transposed operand, a float
-accumulator, a miscount), built with gcc into a temporary directory and run
+accumulator, a miscount, a wrong rounding), built with gcc into a temporary directory and run
 through the same pins as the real oracle.  Every mutant must fail at least
 one pin.  CPU only; the real oracle source is never modified.
 """
@@ -42,6 +42,17 @@ MUTANTS = {
     "miscounted_reads": ("reads += 2 * K;", "reads += K;"),
     "gelu_wrong_scale": ("erf(x / sqrt(2.0))", "erf(x / 2.0)"),
     "bias_by_row": ("(bias ? (double)bias[j] : 0.0)", "(bias ? (double)bias[i % N] : 0.0)"),
+    "bf16_truncates": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;"),
+    "bf16_ties_away": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    "bf16_ties_down": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0x7FFFu;"),
+    "bf16_low_bits_kept": ("u &= 0xFFFF0000u;", "u &= 0xFFFFFFFFu;"),
+    "bf16_mask_too_wide": ("u &= 0xFFFF0000u;", "u &= 0xFFFE0000u;"),
+    "bf16_a_not_rounded": ("const float a = round_bf16((float)op_a(A, lda, transA, i, k));",
+                           "const float a = (float)op_a(A, lda, transA, i, k);"),
+    "bf16_b_not_rounded": ("const float b = round_bf16((float)op_b(B, ldb, transB, k, j));",
+                           "const float b = (float)op_b(B, ldb, transB, k, j);"),
+    "bf16_b_transposed": ("round_bf16((float)op_b(B, ldb, transB, k, j))",
+                          "round_bf16((float)op_b(B, ldb, 1 - transB, k, j))"),
 }
 
 
@@ -58,6 +69,8 @@ def _all_pins(orc):
     yield "counts", lambda: pins.pin_counts(
         lambda A, B, M, N, K: orc.gemm(A, B, M, N, K, 0, 0, with_stats=True))
     yield "epilogue", lambda: pins.pin_epilogue(orc.epilogue)
+    yield "bf16_round", lambda: pins.pin_bf16_rounding(orc.round_bf16)
+    yield "bf16_gemm", lambda: pins.pin_bf16_gemm(orc.gemm_bf16)
 
 
 def _caught(orc):

@@ -134,3 +134,33 @@ def test_batched_equals_block_diagonal_product(oracle, ta, tb, gap, shared):
 
 def test_epilogue(oracle):
     pins.pin_epilogue(oracle.epilogue)
+
+
+def test_bf16_rounding(oracle):
+    pins.pin_bf16_rounding(oracle.round_bf16)
+
+
+def test_bf16_product(oracle):
+    pins.pin_bf16_gemm(oracle.gemm_bf16)
+
+
+def test_bf16_entries_match_full_product(oracle):
+    w = gi.WORKLOADS["R"]
+    A, B = w.make_a(), w.make_b()
+    rows, cols = gi.sample_entries(w.M, w.N, 400)
+    full = oracle.gemm_bf16(A, B, w.M, w.N, w.K, w.transA, w.transB)
+    got = oracle.entries_bf16(A, B, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
+    assert np.array_equal(got, full[rows, cols])
+
+
+def test_bf16_differs_from_f32_by_operand_rounding(oracle):
+    """Uniform(-1, 1) operands: the mixed-precision product moves off the
+    FP32 product by about the operands' relative rounding (at most 2^-9
+    each), far more than the FP32 tolerance, so parity tests against the
+    wrong reference would fail."""
+    w = gi.WORKLOADS["S64"]
+    A, B = w.make_a(), w.make_b()
+    exact = oracle.gemm(A, B, w.M, w.N, w.K)
+    mixed = oracle.gemm_bf16(A, B, w.M, w.N, w.K)
+    rel = np.linalg.norm(mixed - exact) / np.linalg.norm(exact)
+    assert 1e-4 < rel < 2 * 2.0 ** -9
