@@ -19,6 +19,9 @@ Besides the metric the line carries:
                 inputs, for comparison;
   parity        a sampled check of the timed result against the oracle.
 
+``--algo bf16`` times the mixed-precision entry point instead (operands
+rounded to bf16, FP32 sums) against the dense bf16 matrix peak (2.5 PFLOP/s).
+
 ``--copy-probe`` instead runs a plain device copy of known size, the
 scale reference for the HBM byte counters.  ``--gpus`` above 1 exits:
 this benchmark measures one GPU.
@@ -37,6 +40,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 MI355X_FP32_PEAK_TFLOPS = 157.3   # 256 CU x 2.4 GHz x 256 FLOP/clk/CU (matrix and packed vector)
+MI355X_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak (published; no structured sparsity)
 MI355X_HBM_TBPS = 8.0
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -125,8 +129,9 @@ def _lscpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, target_s: float = 12.0) -> dict:
-    """The oracle, as it stands, on a row panel of the workload's product."""
+def cpu_baseline(w, target_s: float = 12.0, mixed: bool = False) -> dict:
+    """The oracle, as it stands, on a row panel of the workload's product
+    (its mixed-precision function when ``mixed``)."""
     import numpy as np
     import oracle
     orc = oracle.load()
@@ -136,7 +141,8 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
         # a panel of `rows` rows of C: the same product restricted to A's first rows
         a_panel = A[:, :rows] if w.transA else A[:rows]
         t0 = time.perf_counter()
-        orc.gemm(np.ascontiguousarray(a_panel), B, rows, w.N, w.K, w.transA, w.transB)
+        fn = orc.gemm_bf16 if mixed else orc.gemm
+        fn(np.ascontiguousarray(a_panel), B, rows, w.N, w.K, w.transA, w.transB)
         return time.perf_counter() - t0
 
     probe_rows = max(1, min(w.M, 16))
@@ -146,7 +152,8 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
     tflops = gemm_flops(rows, w.N, w.K) / t / 1e12
     return {"value": tflops, "unit": "TFLOPS", "cores": orc.threads(), "kind": "oracle",
             "sample": f"first {rows} of {w.M} rows of C ({w.name}: {w.M}x{w.N}x{w.K}), "
-                      f"{t:.1f} s, FP64-accumulating triple loop, OpenMP over rows",
+                      f"{t:.1f} s, FP64-accumulating triple loop"
+                      f"{' on bf16-rounded operands' if mixed else ''}, OpenMP over rows",
             "host_cpu": _lscpu_model(), "os_cpu_count": os.cpu_count(),
             "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
@@ -170,7 +177,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--algo", default="auto",
-                    choices=["auto", "mfma", "mfma128", "mfma64", "fma", "tiled", "naive"])
+                    choices=["auto", "mfma", "mfma128", "mfma64", "fma", "tiled", "naive", "bf16"],
+                    help="kernel family; bf16 times the mixed-precision entry point "
+                         "(operands rounded to bf16, FP32 sums)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -205,13 +214,17 @@ def main(argv=None) -> int:
     dB = torch.from_numpy(B).cuda()
     dC = torch.from_numpy(C).cuda()
     stream = torch.cuda.current_stream()
-    algo_id = g.ALGOS[args.algo]
+    mixed = args.algo == "bf16"
+    algo_id = g.ALGOS["auto" if mixed else args.algo]
 
     batched = w.batch > 1
     if batched and args.algo not in ("auto", "mfma"):
         print("batched workloads run on the MFMA path only", file=sys.stderr)
         return 2
     fused = args.epilogue != "none"
+    if mixed and batched:
+        print("the mixed-precision entry point takes single products", file=sys.stderr)
+        return 2
     if fused and (batched or args.algo not in ("auto", "mfma")):
         print("the fused epilogue runs single products on the MFMA path", file=sys.stderr)
         return 2
@@ -224,6 +237,9 @@ def main(argv=None) -> int:
             st = g.gemm_f32_bias_act(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
                                      dC.data_ptr(), w.ldc_, w.transA, w.transB, dbias.data_ptr(),
                                      act, stream.cuda_stream)
+        elif mixed and algo == algo_id:
+            st = g.gemm_f32_bf16(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
+                                 dC.data_ptr(), w.ldc_, w.transA, w.transB, stream.cuda_stream)
         elif batched:
             st = g.gemm_f32_strided_batched(
                 w.M, w.N, w.K, dA.data_ptr(), w.lda_, w.stride_a, dB.data_ptr(), w.ldb_,
@@ -252,7 +268,8 @@ def main(argv=None) -> int:
             a0 = A[last, :w.a_dims[0] * w.lda_].reshape(w.a_dims[0], w.lda_)
             b0 = B if w.shared_b else B[last, :w.b_dims[0] * w.ldb_].reshape(w.b_dims[0], w.ldb_)
             c0 = c0[last, :w.M * w.ldc_].reshape(w.M, w.ldc_)
-        ref = oracle.load().entries(a0, b0, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
+        entries = oracle.load().entries_bf16 if mixed else oracle.load().entries
+        ref = entries(a0, b0, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
         if fused:
             ref = oracle.load().epilogue((ref + bias[cols].astype(np.float64))[None, :], None,
                                          act)[0]
@@ -262,8 +279,9 @@ def main(argv=None) -> int:
                   "ok": bool(np.all(ratio <= 1.0))}
 
     kernel = "gemm_f32_" + ("mfma" if args.algo in ("auto", "mfma128", "mfma64") else args.algo)
-    roofline = {"bound": "mfma", "achieved": value, "peak": MI355X_FP32_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": value / MI355X_FP32_PEAK_TFLOPS,
+    peak = MI355X_BF16_PEAK_TFLOPS if mixed else MI355X_FP32_PEAK_TFLOPS
+    roofline = {"bound": "mfma", "achieved": value, "peak": peak,
+                "unit": "TFLOP/s", "frac": value / peak,
                 "traffic": read_traffic(kernel, name),
                 "kernel": kernel, "flops_per_launch": flops,
                 "compulsory_bytes": compulsory_bytes(w.M, w.N, w.K) * w.batch}
@@ -305,6 +323,21 @@ def main(argv=None) -> int:
                                                   "ms": tms},
                    "gemm_f32 without epilogue": {"tflops": flops / (plain * 1e-3) / 1e12,
                                                  "ms": plain}}
+    elif not args.no_context and mixed:
+        ta = dA[:, :w.a_dims[1]]
+        tb = dB[:, :w.b_dims[1]]
+        ta = ta.t() if w.transA else ta
+        tb = tb.t() if w.transB else tb
+        ha, hb = ta.to(torch.bfloat16), tb.to(torch.bfloat16)
+        out16 = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        t16 = _timed(lambda: torch.mm(ha, hb, out=out16), 20, 5)
+        t32 = _timed(lambda: torch.mm(ta, tb, out=out), 20, 5)
+        mine = _timed(lambda: step(g.ALGOS["mfma"]), 20, 5)
+        context = {"torch.mm bf16 (operands pre-converted, bf16 output)":
+                   {"tflops": flops / (t16 * 1e-3) / 1e12, "ms": t16},
+                   "torch.mm f32": {"tflops": flops / (t32 * 1e-3) / 1e12, "ms": t32},
+                   "gemm_f32 (FP32 MFMA)": {"tflops": flops / (mine * 1e-3) / 1e12, "ms": mine}}
     elif not args.no_context:
         context = {}
         for other in ("mfma", "fma", "tiled", "naive"):
@@ -330,10 +363,11 @@ def main(argv=None) -> int:
 
     cpu = None
     if not args.no_cpu_baseline and not batched:
-        cpu = cpu_baseline(w)
+        cpu = cpu_baseline(w, mixed=mixed)
 
     line = {
-        "metric": "FP32 GEMM TFLOPS (2MNK/s) and % of MI355X FP32 peak at N=4096",
+        "metric": ("mixed-precision GEMM TFLOPS (2MNK/s; bf16 operands, FP32 sums)" if mixed else
+                   "FP32 GEMM TFLOPS (2MNK/s) and % of MI355X FP32 peak at N=4096"),
         "value": value,
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -343,14 +377,14 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if mixed else "f32",
         "data": "synthetic",
         "config": {"workload": name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
                    "lda": w.lda_,
                    "ldb": w.ldb_, "ldc": w.ldc_, "transA": w.transA, "transB": w.transB,
                    "inputs": w.description, "seeds": [w.seed_a, w.seed_b],
                    "algo": args.algo, "epilogue": args.epilogue, "parallelism": "single GPU"},
-        "pct_of_peak": 100.0 * value / MI355X_FP32_PEAK_TFLOPS,
+        "pct_of_peak": 100.0 * value / peak,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "context": context,

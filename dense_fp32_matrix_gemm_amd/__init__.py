@@ -10,12 +10,13 @@ current stream, and calls the library.  PyTorch owns memory and streams.
 
 from __future__ import annotations
 
-from ._lib import (ACT_GELU, ACT_NONE, ALGOS, LibraryNotBuilt, gemm_f32, gemm_f32_bias_act,
+from ._lib import (ACT_GELU, ACT_NONE, ALGOS, LibraryNotBuilt, gemm_f32, gemm_f32_bf16,
+                   gemm_f32_bias_act,
                    gemm_f32_ex, gemm_f32_naive, gemm_f32_strerror, gemm_f32_strided_batched,
                    gemm_f32_version, library_path, load)
 
 __all__ = ["ACT_GELU", "ACT_NONE", "ALGOS", "GemmError", "LibraryNotBuilt", "bmm", "gemm_f32",
-           "gemm_f32_bias_act", "gemm_f32_ex", "linear",
+           "gemm_f32_bf16", "gemm_f32_bias_act", "gemm_f32_ex", "linear",
            "gemm_f32_naive", "gemm_f32_strerror", "gemm_f32_strided_batched",
            "gemm_f32_version", "library_path", "load", "matmul", "operand_layout"]
 

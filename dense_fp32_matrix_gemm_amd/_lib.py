@@ -29,6 +29,7 @@ SIGNATURES = {
                                         _ptr, _i64, _i64, _i64, _int, _int, _ptr]),
     "gemm_f32_bias_act": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                  _ptr, _int, _ptr]),
+    "gemm_f32_bf16": (_int, _GEMM_ARGS),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
     "gemm_f32_version": (_int, []),
 }
@@ -93,6 +94,11 @@ ACT_NONE, ACT_GELU = 0, 1
 def gemm_f32_bias_act(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, bias, act, stream) -> int:
     return _call("gemm_f32_bias_act", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, bias, act,
                  stream)
+
+
+def gemm_f32_bf16(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream) -> int:
+    """C = op(A) . op(B) with operands rounded to bf16, FP32 sums and output."""
+    return _call("gemm_f32_bf16", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream)
 
 
 def gemm_f32_strerror(status: int) -> str:

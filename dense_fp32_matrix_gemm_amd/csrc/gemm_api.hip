@@ -170,6 +170,19 @@ int gemm_f32_bias_act(int64_t M, int64_t N, int64_t K, const float *A, int64_t l
     return err == hipSuccess ? 0 : int(err);
 }
 
-int gemm_f32_version(void) { return 10200; }
+int gemm_f32_bf16(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                  const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
+                  int transB, void *stream)
+{
+    const int bad = validate(M, N, K, A, lda, B, ldb, C, ldc, transA, transB);
+    if (bad) return bad;
+    if (M == 0 || N == 0) return 0;
+    const Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = K == 0 ? gemmf32::launch_zero_fill(p, s) : gemmf32::launch_bf16(p, s);
+    return err == hipSuccess ? 0 : int(err);
+}
+
+int gemm_f32_version(void) { return 10300; }
 
 }  // extern "C"

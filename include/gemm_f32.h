@@ -135,6 +135,26 @@ int gemm_f32_bias_act(int64_t M, int64_t N, int64_t K,
                       int transA, int transB,
                       const float *bias, int act, void *stream);
 
+/* Mixed precision: C = op(A) . op(B) with each operand element rounded to
+ * bf16 (8 significant bits, the exponent range of FP32; round to nearest,
+ * ties to even) before it is multiplied, the products added in FP32 and C
+ * written in FP32.  A, B and C are FP32 arrays as for gemm_f32; the rounding
+ * happens on the way into the kernel, and neither operand is modified.
+ * This is the Smallem page's mixed precision ("Rendre le GPU rapide",
+ * section "Les Tensor Cores"): only the operands of the multiplication are
+ * rounded to 16 bits; sums and tensors stay FP32.  Results agree with the
+ * exact product of the rounded operands to within 1e-6*K + 1e-5*|C|
+ * elementwise for operands of magnitude <= 1, and equal it exactly when
+ * every rounded operand is an integer and every partial sum of the integer
+ * products has magnitude below 2^24 (for instance integers in [-8, 8] with
+ * K <= 2^18).  Storage, ownership, quick returns and status codes as for
+ * gemm_f32.  Runs on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16). */
+int gemm_f32_bf16(int64_t M, int64_t N, int64_t K,
+                  const float *A, int64_t lda,
+                  const float *B, int64_t ldb,
+                  float *C, int64_t ldc,
+                  int transA, int transB, void *stream);
+
 /* A static, human-readable description of a return value (never NULL).
  * Messages for -i name gemm_f32's arguments. */
 const char *gemm_f32_strerror(int status);

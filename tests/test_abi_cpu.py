@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert g.gemm_f32_version() == 10200
+    assert g.gemm_f32_version() == 10300
 
 
 def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
@@ -64,7 +64,7 @@ def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
     return getattr(g, fn)(*args)
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_naive", "gemm_f32_ex"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_naive", "gemm_f32_ex", "gemm_f32_bf16"])
 @pytest.mark.parametrize("kwargs,code", [
     (dict(M=-1), -1), (dict(N=-1), -2), (dict(K=-1), -3),
     (dict(M=BIG), -1), (dict(N=BIG), -2), (dict(K=BIG), -3),
@@ -92,6 +92,7 @@ def test_quick_return_without_launch(kwargs):
     """M == 0 or N == 0: nothing to write, status 0, no HIP call (works without a GPU)."""
     assert call(**kwargs) == 0
     assert call(fn="gemm_f32_ex", algo=1, **kwargs) == 0
+    assert call(fn="gemm_f32_bf16", **kwargs) == 0
 
 
 def test_strerror_is_total():
@@ -133,7 +134,7 @@ def test_operand_layout_from_strides():
 def test_header_is_plain_c():
     """The public header compiles as C with no HIP headers on the include path."""
     import subprocess
-    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10200 ? 0 : 1;}\n"
+    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10300 ? 0 : 1;}\n"
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
                        input=src, capture_output=True, text=True)
