@@ -177,7 +177,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--algo", default="auto",
-                    choices=["auto", "mfma", "mfma128", "mfma64", "fma", "tiled", "naive", "bf16"],
+                    choices=["auto", "mfma", "mfma256", "mfma128", "mfma64", "fma", "tiled", "naive", "bf16"],
                     help="kernel family; bf16 times the mixed-precision entry point "
                          "(operands rounded to bf16, FP32 sums)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -278,7 +278,7 @@ def main(argv=None) -> int:
         parity = {"entries": int(rows.size), "max_err_over_bound": float(np.max(ratio)),
                   "ok": bool(np.all(ratio <= 1.0))}
 
-    kernel = "gemm_f32_" + ("mfma" if args.algo in ("auto", "mfma128", "mfma64") else args.algo)
+    kernel = "gemm_f32_" + ("mfma" if args.algo in ("auto", "mfma256", "mfma128", "mfma64") else args.algo)
     peak = MI355X_BF16_PEAK_TFLOPS if mixed else MI355X_FP32_PEAK_TFLOPS
     roofline = {"bound": "mfma", "achieved": value, "peak": peak,
                 "unit": "TFLOP/s", "frac": value / peak,

@@ -48,7 +48,7 @@ int run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
 {
     const int bad = validate(M, N, K, A, lda, B, ldb, C, ldc, transA, transB);
     if (bad) return bad;
-    if (algo < GEMM_F32_ALGO_AUTO || algo > GEMM_F32_ALGO_MFMA_TILE64) return -kArgAlgo;
+    if (algo < GEMM_F32_ALGO_AUTO || algo > GEMM_F32_ALGO_MFMA_TILE256) return -kArgAlgo;
     if (M == 0 || N == 0) return 0;  // nothing to write
 
     const Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
@@ -63,6 +63,7 @@ int run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
         case GEMM_F32_ALGO_FMA: err = gemmf32::launch_fma(p, s); break;
         case GEMM_F32_ALGO_MFMA_TILE128: err = gemmf32::launch_mfma(p, s, 128); break;
         case GEMM_F32_ALGO_MFMA_TILE64: err = gemmf32::launch_mfma(p, s, 64); break;
+        case GEMM_F32_ALGO_MFMA_TILE256: err = gemmf32::launch_mfma(p, s, 256); break;
         case GEMM_F32_ALGO_MFMA:
         case GEMM_F32_ALGO_AUTO:
         default: err = gemmf32::launch_mfma(p, s, 0); break;

@@ -34,7 +34,7 @@ struct Problem {
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_tiled(const Problem &p, hipStream_t stream);
 hipError_t launch_fma(const Problem &p, hipStream_t stream);
-// tile: 0 chooses by problem size; 128 or 64 forces that tile edge.
+// tile: 0 chooses by problem size; 256 (256 x 128), 128 or 64 forces that tile.
 hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
 // Operands rounded to bf16 (nearest, ties to even), bf16 matrix-core
 // products, FP32 sums and output.  Ignores batch, bias and act.

@@ -70,7 +70,8 @@ enum gemm_f32_algo {
     GEMM_F32_ALGO_TILED = 3, /* T x T LDS tiles, one output per thread (section 3.3) */
     GEMM_F32_ALGO_NAIVE = 4, /* one lane per output, operands from global memory (3.1) */
     GEMM_F32_ALGO_MFMA_TILE128 = 5, /* MFMA with the 128 x 128 tile forced */
-    GEMM_F32_ALGO_MFMA_TILE64 = 6   /* MFMA with the 64 x 64 (split-k-group) tile forced */
+    GEMM_F32_ALGO_MFMA_TILE64 = 6,  /* MFMA with the 64 x 64 (split-k-group) tile forced */
+    GEMM_F32_ALGO_MFMA_TILE256 = 7  /* MFMA with the 256 x 128 tile forced */
 };
 
 /* C = op(A) . op(B) on the fastest path (GEMM_F32_ALGO_AUTO). */

@@ -82,7 +82,7 @@ def test_invalid_arguments(fn, kwargs, code):
 
 
 def test_invalid_algo():
-    assert call(fn="gemm_f32_ex", algo=7) == -13
+    assert call(fn="gemm_f32_ex", algo=8) == -13
     assert call(fn="gemm_f32_ex", algo=-1) == -13
 
 

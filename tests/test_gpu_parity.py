@@ -12,8 +12,8 @@ import parity as P
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["mfma", "mfma128", "mfma64", "fma", "tiled", "naive"]
-FAST_ALGOS = ["mfma128", "mfma64", "fma"]
+ALGOS = ["mfma", "mfma256", "mfma128", "mfma64", "fma", "tiled", "naive"]
+FAST_ALGOS = ["mfma256", "mfma128", "mfma64", "fma"]
 
 _ref_cache = {}
 
