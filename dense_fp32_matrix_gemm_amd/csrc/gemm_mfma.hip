@@ -33,11 +33,13 @@
 //    k = 4 + u for the four MFMAs u = 0..3.  Both operands use the same map,
 //    so every pair (a_ik, b_kj) meets exactly once, and a k-contiguous
 //    operand is read with one 16-byte LDS read per lane per 4 MFMAs.
-//  * Accumulation: each stage's 32 k values are summed into a fresh MFMA
-//    accumulator (the first MFMA of the stage takes a zero addend) and then
-//    added into the running tile.  The matrix core adds one product at a
-//    time in FP32, so without this the relative error of a K = 8192 product
-//    grows past 1e-6; with it the error stays near 3e-7.
+//  * Accumulation: each run of 128 k values (192 on the 256 x 128 tile) is
+//    summed into a fresh MFMA accumulator (the first MFMA of the run takes a
+//    zero addend) and then added into the running tile.  The matrix core
+//    adds one product at a time in FP32, so without this the relative error
+//    of a K = 8192 product grows past 1e-6; with it the error stays near
+//    2.5e-7.  Longer runs mean fewer folds (each one drains the wave's MFMA
+//    chain) at a small cost in accuracy.
 //  * Launch order: workgroups are dealt round-robin to the 8 XCDs, each with
 //    its own L2.  The tile index is remapped so that each XCD receives a
 //    contiguous run of tiles, and that run is walked GROUP_M tile-rows at a
@@ -117,7 +119,8 @@ struct Config {
     static_assert(BK % 8 == 0, "stages are whole 8-k fragment groups");
     static_assert((BK / 8) % KSPLIT_ == 0, "k-slices share a stage's groups evenly");
     static_assert(KSPLIT_ == 1 || KSPLIT_ == 2 || KSPLIT_ == 4, "k-slices reduce as a binary tree");
-    static_assert(NBUF_ >= 2 && NBUF_ <= 4 && NBUF_ % FOLD_ == 0, "2-4 stage buffers, whole chunks");
+    static_assert(NBUF_ >= 2 && NBUF_ <= 4 && (NBUF_ % FOLD_ == 0 || FOLD_ % NBUF_ == 0),
+                  "2-4 stage buffers; a chunk divides, or is a multiple of, the buffer cycle");
     static_assert(KSPLIT_ == 1 || BM * BN <= (BM + BN) * BK,
                   "a k-slice's partial tile fits in one stage buffer for the reduction");
 };
@@ -390,9 +393,11 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         dma(buf0, 0);
         if (NB > 2 && 1 < full) dma(bufp(Int<1 % NB>{}), 1);
         if (NB > 3 && 2 < full) dma(bufp(Int<2 % NB>{}), 2);
-        // NB stages per trip so each buffer is a compile-time choice.
-        for (int s = 0; s < full; s += NB) {
-            unroll_for<NB>([&](auto bi) {
+        // TRIP stages per trip (a multiple of NB and of FOLD) so that each
+        // buffer and each chunk boundary is a compile-time choice.
+        constexpr int TRIP = NB > FOLD ? NB : FOLD;
+        for (int s = 0; s < full; s += TRIP) {
+            unroll_for<TRIP>([&](auto bi) {
                 constexpr int b = decltype(bi)::value;
                 const int st = s + b;
                 if (st < full) {
@@ -406,7 +411,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                         wait_vm<(NB - 2) * D>();
                     __syncthreads();
                     if (st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
-                    compute(bufp(Int<b>{}), nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{});
+                    compute(bufp(Int<b % NB>{}), nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{});
                 }
             });
         }
@@ -487,21 +492,21 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 }
 
 #ifndef GEMM_MFMA_CONFIG
-#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 2, 1
+#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 4, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_CONFIG
 #define GEMM_MFMA_SMALL_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4, 0
 #endif
 #ifndef GEMM_MFMA_HUGE_CONFIG
-#define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 8, 3, 1, 1, 3, 3, 1
+#define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 8, 3, 1, 1, 3, 6, 1
 #endif
 #ifndef GEMM_MFMA_KK_CONFIG
-#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 4, 1
+#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1
 #endif
 using Default = Config<GEMM_MFMA_CONFIG>;
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
 // 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU (three 48 KB
-// stage buffers, two stages of copies in flight, 96-k accumulation chunks).
+// stage buffers, two stages of copies in flight, 192-k accumulation chunks).
 // A quarter fewer bytes copied into LDS per flop than the 128 x 128 tile:
 // on 4096^3 136 vs 134 TFLOP/s.  Needs enough tiles to fill every CU twice.
 using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
