@@ -31,7 +31,6 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import glob
 import json
 import os
 import sys
@@ -70,10 +69,24 @@ def compulsory_bytes(M: int, N: int, K: int) -> int:
     return 4 * (M * K + K * N + M * N)
 
 
-def source_digest() -> str:
-    """Hash of the HIP sources; counter summaries are valid only for this digest."""
+# The sources each kernel family is compiled from (its own file plus the
+# shared headers); a counter summary stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "gemm_f32_mfma": ["gemm_mfma.hip", "tile_common.hpp", "gemm_internal.hpp"],
+    "gemm_f32_fma": ["gemm_fma.hip", "tile_common.hpp", "gemm_internal.hpp"],
+    "gemm_f32_tiled": ["gemm_simple.hip", "gemm_internal.hpp"],
+    "gemm_f32_naive": ["gemm_simple.hip", "gemm_internal.hpp"],
+    "gemm_f32_bf16": ["gemm_bf16.hip", "tile_common.hpp", "gemm_internal.hpp"],
+}
+
+
+def source_digest(kernel: str = "gemm_f32_mfma") -> str:
+    """Hash of the sources of one kernel family; counter summaries are valid
+    only for this digest."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "dense_fp32_matrix_gemm_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "dense_fp32_matrix_gemm_amd", "csrc")
+    for name in sorted(KERNEL_SOURCES[kernel]):
+        p = os.path.join(csrc, name)
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -92,7 +105,7 @@ def read_traffic(kernel: str, workload: str):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("source_digest") != source_digest():
+    if kernel not in KERNEL_SOURCES or fields.get("source_digest") != source_digest(kernel):
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))

@@ -36,9 +36,10 @@ hipError_t launch_tiled(const Problem &p, hipStream_t stream);
 hipError_t launch_fma(const Problem &p, hipStream_t stream);
 // tile: 0 chooses by problem size; 256 (256 x 128), 128 or 64 forces that tile.
 hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
+// tile: 0 chooses by problem size; 256 (256 x 256) or 128 forces that tile.
 // Operands rounded to bf16 (nearest, ties to even), bf16 matrix-core
 // products, FP32 sums and output.  Ignores batch, bias and act.
-hipError_t launch_bf16(const Problem &p, hipStream_t stream);
+hipError_t launch_bf16(const Problem &p, hipStream_t stream, int tile = 0);
 // C := act(0 + bias[j]) over M x N (the empty sum, K == 0), for every
 // product of the batch.  Assumes M, N >= 1.
 hipError_t launch_zero_fill(const Problem &p, hipStream_t stream);

@@ -52,8 +52,10 @@ def run_bf16(M, N, K, A, B, C, ta, tb, label="", offsets=(0, 0, 0)):
     return dC.cpu().numpy()[offsets[2]:].reshape(C.shape)
 
 
+# The last shape has enough 256 x 256 tiles (12 x 12) to take the large
+# tile, with partial tiles in every dimension and a partial last stage.
 SHAPES = [(1, 1, 1), (37, 45, 29), (128, 128, 32), (129, 257, 95), (300, 200, 512),
-          (1000, 1000, 1000), (2049, 700, 77)]
+          (1000, 1000, 1000), (2049, 700, 77), (3001, 2817, 100)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
