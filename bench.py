@@ -198,6 +198,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--epilogue", default="none", choices=["none", "bias", "gelu"],
                     help="time the fused C = act(A.B + bias) entry point instead")
+    ap.add_argument("--splitk", type=int, default=0,
+                    help="time gemm_f32_splitk with this many runs of k (partials plus their sum)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -241,12 +243,22 @@ def main(argv=None) -> int:
     if fused and (batched or args.algo not in ("auto", "mfma")):
         print("the fused epilogue runs single products on the MFMA path", file=sys.stderr)
         return 2
+    splitk = args.splitk > 0
+    if splitk and (batched or fused or mixed or args.algo not in ("auto", "mfma")):
+        print("--splitk times single FP32 products on the MFMA path", file=sys.stderr)
+        return 2
+    ws_bytes = g.gemm_f32_splitk_workspace_size(w.M, w.N, w.K, args.splitk) if splitk else 0
+    dws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda") if splitk else None
     bias = gi.stored_matrix(2003, 1, w.N, dist="n002")[0] if fused else None
     dbias = torch.from_numpy(bias).cuda() if fused else None
     act = g.ACT_GELU if args.epilogue == "gelu" else g.ACT_NONE
 
-    def step(algo=algo_id):
-        if fused:
+    def step(algo=algo_id, plain=False):
+        if splitk and not plain:
+            st = g.gemm_f32_splitk(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
+                                   dC.data_ptr(), w.ldc_, w.transA, w.transB, args.splitk,
+                                   dws.data_ptr(), ws_bytes, stream.cuda_stream)
+        elif fused:
             st = g.gemm_f32_bias_act(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
                                      dC.data_ptr(), w.ldc_, w.transA, w.transB, dbias.data_ptr(),
                                      act, stream.cuda_stream)
@@ -336,6 +348,17 @@ def main(argv=None) -> int:
                                                   "ms": tms},
                    "gemm_f32 without epilogue": {"tflops": flops / (plain * 1e-3) / 1e12,
                                                  "ms": plain}}
+    elif not args.no_context and splitk:
+        plain = _timed(lambda: step(g.ALGOS["mfma"], plain=True), 50, 20)
+        ta = dA[:, :w.a_dims[1]]
+        tb = dB[:, :w.b_dims[1]]
+        ta = ta.t() if w.transA else ta
+        tb = tb.t() if w.transB else tb
+        out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        tms = _timed(lambda: torch.mm(ta, tb, out=out), 50, 20)
+        context = {"gemm_f32 (one product)": {"tflops": flops / (plain * 1e-3) / 1e12, "ms": plain},
+                   "torch.mm": {"tflops": flops / (tms * 1e-3) / 1e12, "ms": tms},
+                   "workspace_bytes": ws_bytes}
     elif not args.no_context and mixed:
         ta = dA[:, :w.a_dims[1]]
         tb = dB[:, :w.b_dims[1]]
@@ -396,7 +419,8 @@ def main(argv=None) -> int:
                    "lda": w.lda_,
                    "ldb": w.ldb_, "ldc": w.ldc_, "transA": w.transA, "transB": w.transB,
                    "inputs": w.description, "seeds": [w.seed_a, w.seed_b],
-                   "algo": args.algo, "epilogue": args.epilogue, "parallelism": "single GPU"},
+                   "algo": args.algo, "epilogue": args.epilogue, "splitk": args.splitk,
+                   "parallelism": "single GPU"},
         "pct_of_peak": 100.0 * value / peak,
         "roofline": roofline,
         "cpu_baseline": cpu,

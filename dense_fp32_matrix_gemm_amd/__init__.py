@@ -12,13 +12,16 @@ from __future__ import annotations
 
 from ._lib import (ACT_GELU, ACT_NONE, ALGOS, LibraryNotBuilt, gemm_f32, gemm_f32_bf16,
                    gemm_f32_bias_act,
-                   gemm_f32_ex, gemm_f32_naive, gemm_f32_strerror, gemm_f32_strided_batched,
-                   gemm_f32_version, library_path, load)
+                   gemm_f32_ex, gemm_f32_naive, gemm_f32_splitk, gemm_f32_splitk_workspace_size,
+                   gemm_f32_strerror, gemm_f32_strided_batched, gemm_f32_version, library_path,
+                   load)
 
 __all__ = ["ACT_GELU", "ACT_NONE", "ALGOS", "GemmError", "LibraryNotBuilt", "bmm", "gemm_f32",
            "gemm_f32_bf16", "gemm_f32_bias_act", "gemm_f32_ex", "linear",
-           "gemm_f32_naive", "gemm_f32_strerror", "gemm_f32_strided_batched",
-           "gemm_f32_version", "library_path", "load", "matmul", "operand_layout"]
+           "gemm_f32_naive", "gemm_f32_splitk", "gemm_f32_splitk_workspace_size",
+           "gemm_f32_strerror", "gemm_f32_strided_batched",
+           "gemm_f32_version", "library_path", "load", "matmul", "matmul_splitk",
+           "operand_layout"]
 
 
 class GemmError(RuntimeError):
@@ -140,6 +143,43 @@ def linear(x, w, bias=None, activation=None, out=None, stream=None):
         stream = torch.cuda.current_stream(x.device).cuda_stream
     st = gemm_f32_bias_act(M, N, K, x.data_ptr(), lda, w.data_ptr(), ldb, out.data_ptr(), ldc,
                            ta, tb, None if bias is None else bias.data_ptr(), act, stream)
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def matmul_splitk(a, b, splits: int, out=None, workspace=None, stream=None):
+    """out = a @ b as ``splits`` partial products over runs of k and their sum
+    (gemm_f32_splitk).  ``workspace`` is a float32 device tensor of at least
+    gemm_f32_splitk_workspace_size bytes; if None one is allocated here."""
+    import torch
+
+    if a.dtype != torch.float32 or b.dtype != torch.float32:
+        raise TypeError("matmul_splitk takes float32 tensors")
+    if not (a.is_cuda and b.is_cuda):
+        raise ValueError("matmul_splitk takes device tensors")
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    if out.shape != (M, N) or out.dtype != torch.float32 or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be an M x N float32 tensor with unit column stride")
+    need = gemm_f32_splitk_workspace_size(M, N, K, splits)
+    if need < 0:
+        raise GemmError(int(need))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=a.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ta, lda = operand_layout(a)
+    tb, ldb = operand_layout(b)
+    ldc = max(out.stride(0), N, 1) if M > 1 else max(N, 1)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    st = gemm_f32_splitk(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
+                         ta, tb, splits, ws_ptr, ws_bytes, stream)
     if st != 0:
         raise GemmError(st)
     return out

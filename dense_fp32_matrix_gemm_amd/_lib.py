@@ -31,6 +31,9 @@ SIGNATURES = {
     "gemm_f32_bias_act": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                  _ptr, _int, _ptr]),
     "gemm_f32_bf16": (_int, _GEMM_ARGS),
+    "gemm_f32_splitk": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
+                               _i64, _ptr, _i64, _ptr]),
+    "gemm_f32_splitk_workspace_size": (_i64, [_i64, _i64, _i64, _i64]),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
     "gemm_f32_version": (_int, []),
 }
@@ -100,6 +103,19 @@ def gemm_f32_bias_act(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, bias, act
 def gemm_f32_bf16(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream) -> int:
     """C = op(A) . op(B) with operands rounded to bf16, FP32 sums and output."""
     return _call("gemm_f32_bf16", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream)
+
+
+def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, splits, workspace,
+                    workspace_bytes, stream) -> int:
+    """C = op(A) . op(B) as ``splits`` partial products over runs of k plus
+    their fixed-order sum; ``workspace`` is a device address of at least
+    ``gemm_f32_splitk_workspace_size`` bytes (0/None when that is 0)."""
+    return _call("gemm_f32_splitk", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, splits,
+                 workspace, workspace_bytes, stream)
+
+
+def gemm_f32_splitk_workspace_size(M, N, K, splits) -> int:
+    return int(load().gemm_f32_splitk_workspace_size(M, N, K, splits))
 
 
 def gemm_f32_strerror(status: int) -> str:

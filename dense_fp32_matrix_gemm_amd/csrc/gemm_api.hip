@@ -42,6 +42,19 @@ int validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     return 0;
 }
 
+// Split k: runs of len = ceil(K / splits) rounded up to whole 32-k stages,
+// and the number of non-empty runs that gives (K, splits >= 1).
+int64_t splitk_len(int64_t K, int64_t splits)
+{
+    const int64_t per = (K + splits - 1) / splits;
+    return (per + 31) / 32 * 32;
+}
+int64_t splitk_used(int64_t K, int64_t splits)
+{
+    const int64_t len = splitk_len(K, splits);
+    return (K + len - 1) / len;
+}
+
 int run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
         const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
         int transB, void *stream, int algo)
@@ -114,7 +127,14 @@ const char *gemm_f32_strerror(int status)
     case -kArgLdc: return "invalid argument 9 (ldc): smaller than N, or >= 2^31";
     case -kArgTransA: return "invalid argument 10 (transA): not 0 or 1";
     case -kArgTransB: return "invalid argument 11 (transB): not 0 or 1";
-    case -kArgAlgo: return "invalid argument 13 (algo): unknown kernel family";
+    case -12: return "invalid argument 12 (gemm_f32_splitk: splits < 1 or too large a workspace; "
+                     "gemm_f32_strided_batched: strideC negative or overlapping)";
+    case -kArgAlgo: return "invalid argument 13 (gemm_f32_ex: unknown kernel family; gemm_f32_bias_act: "
+                           "unknown activation; gemm_f32_splitk: workspace NULL; "
+                           "gemm_f32_strided_batched: batch out of range)";
+    case -14: return "invalid argument 14 (gemm_f32_splitk: workspace_bytes below the size needed; "
+                     "gemm_f32_strided_batched: transA not 0 or 1)";
+    case -15: return "invalid argument 15 (gemm_f32_strided_batched: transB not 0 or 1)";
     default: break;
     }
     if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
@@ -184,6 +204,60 @@ int gemm_f32_bf16(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     return err == hipSuccess ? 0 : int(err);
 }
 
-int gemm_f32_version(void) { return 10300; }
+int64_t gemm_f32_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int64_t splits)
+{
+    if (M < 0 || M > kDimLimit) return -1;
+    if (N < 0 || N > kDimLimit) return -2;
+    if (K < 0 || K > kDimLimit) return -3;
+    if (splits < 1 || splits > kDimLimit) return -12;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    const int64_t used = splitk_used(K, splits);
+    if (used == 1) return 0;
+    if (M * N > (int64_t(1) << 60) / used) return -12;  // s_used * M * N * 4 < 2^62
+    return used * M * N * 4;
+}
+
+int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                    const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
+                    int transB, int64_t splits, float *workspace, int64_t workspace_bytes,
+                    void *stream)
+{
+    const int bad = validate(M, N, K, A, lda, B, ldb, C, ldc, transA, transB);
+    if (bad) return bad;
+    const int64_t need = gemm_f32_splitk_workspace_size(M, N, K, splits);
+    if (need < 0) return int(need);
+    if (need > 0 && workspace == nullptr) return -13;
+    if (workspace_bytes < need) return -14;
+    if (M == 0 || N == 0) return 0;
+    Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) {
+        const hipError_t err = gemmf32::launch_zero_fill(p, s);
+        return err == hipSuccess ? 0 : int(err);
+    }
+    if (need == 0) {
+        const hipError_t err = gemmf32::launch_mfma(p, s, 0);
+        return err == hipSuccess ? 0 : int(err);
+    }
+    // Partial s reads op(A)[:, s*len ..] and op(B)[s*len .., :]: a run of k
+    // moves along the stored rows of an operand whose rows hold k (A
+    // untransposed, B transposed), else down its rows.
+    const int64_t len = splitk_len(K, splits);
+    const int64_t used = splitk_used(K, splits);
+    p.K = int(len);
+    p.k_total = int(K);
+    p.stride_a = transA ? len * lda : len;
+    p.stride_b = transB ? len : len * ldb;
+    p.C = workspace;
+    p.ldc = N;
+    p.stride_c = M * N;
+    p.batch = used;
+    hipError_t err = gemmf32::launch_mfma(p, s, 0);
+    if (err == hipSuccess)
+        err = gemmf32::launch_splitk_reduce(workspace, int(used), int(M), int(N), C, ldc, s);
+    return err == hipSuccess ? 0 : int(err);
+}
+
+int gemm_f32_version(void) { return 10400; }
 
 }  // extern "C"

@@ -27,6 +27,10 @@ struct Problem {
     // Fused epilogue: C = act(product + bias[j]); bias may be null.
     const float *bias = nullptr;
     int act = 0;  // 0: none, 1: GELU (erf form)
+    // Split k (MFMA path): when k_total > 0, product b is the partial product
+    // over k in [b*K, min(k_total, (b+1)*K)); the strides move A and B along
+    // k.  0: every product spans K.
+    int k_total = 0;
 };
 
 // Each launcher enqueues its kernel(s) on `stream` and returns
@@ -40,6 +44,10 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
 // Operands rounded to bf16 (nearest, ties to even), bf16 matrix-core
 // products, FP32 sums and output.  Ignores batch, bias and act.
 hipError_t launch_bf16(const Problem &p, hipStream_t stream, int tile = 0);
+// C[i][j] = sum over s < splits, in increasing s, of ws[s*M*N + i*N + j]:
+// the fixed-order sum of split-k partial products (packed M x N each).
+hipError_t launch_splitk_reduce(const float *ws, int splits, int M, int N, float *C, int64_t ldc,
+                                hipStream_t stream);
 // C := act(0 + bias[j]) over M x N (the empty sum, K == 0), for every
 // product of the batch.  Assumes M, N >= 1.
 hipError_t launch_zero_fill(const Problem &p, hipStream_t stream);

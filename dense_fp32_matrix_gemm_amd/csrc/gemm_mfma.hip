@@ -235,13 +235,16 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
             int tiles_m, int tiles_n, int tile_base, int dma_ok, int64_t stride_a,
             int64_t stride_b, int64_t stride_c, int64_t batch_base,
-            const float *__restrict__ bias, int act)
+            const float *__restrict__ bias, int act, int k_total)
 {
     // Strided batch: grid y is the product index.
     const int64_t bz = batch_base + blockIdx.y;
     A += bz * stride_a;
     B += bz * stride_b;
     C += bz * stride_c;
+    // Split k: product bz covers k in [bz * K, min(k_total, (bz + 1) * K)),
+    // its operands already offset by the strides; only the last is shorter.
+    if (k_total > 0) K = int(min(int64_t(K), int64_t(k_total) - bz * K));
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
     constexpr int FM = Cfg::FM, FN = Cfg::FN;
     using TA = Tile<Cfg, BM, A_KC>;
@@ -537,7 +540,8 @@ void dispatch(const Problem &p, hipStream_t s)
             mfma_kernel<Cfg, A_KC, B_KC, VEC>
                 <<<dim3(unsigned(n), unsigned(nb)), dim3(Cfg::threads), 0, s>>>(
                     p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,
-                    int(base), dma_ok, p.stride_a, p.stride_b, p.stride_c, b0, p.bias, p.act);
+                    int(base), dma_ok, p.stride_a, p.stride_b, p.stride_c, b0, p.bias, p.act,
+                    p.k_total);
         }
     }
 }

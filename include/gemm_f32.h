@@ -156,8 +156,41 @@ int gemm_f32_bf16(int64_t M, int64_t N, int64_t K,
                   float *C, int64_t ldc,
                   int transA, int transB, void *stream);
 
+/* Split-k product: C = op(A) . op(B) as in gemm_f32, computed as `splits`
+ * partial products over consecutive runs of k followed by their sum.  The
+ * Smallem page ("Rendre le GPU rapide", section "Ce qui n'a pas marche")
+ * computes the weight gradient as one product per sequence plus a sum,
+ * which ran faster than a single product over all tokens; this is that
+ * decomposition along k for any product.
+ *
+ * The runs are len = ceil(K / splits) rounded up to a multiple of 32, so
+ * s_used = ceil(K / len) <= splits partial products are formed (the last
+ * one shorter).  Partial s (packed M x N, leading dimension N) is written to
+ * workspace + s*M*N; C is then their sum in increasing s, so the result does
+ * not depend on scheduling.  workspace is a device array the caller owns,
+ * of at least gemm_f32_splitk_workspace_size(M, N, K, splits) bytes; its
+ * contents on return are unspecified and it must not overlap A, B or C.  It
+ * may be NULL when that size is 0 (s_used == 1, K == 0, M == 0 or N == 0),
+ * which runs as gemm_f32.  Storage, ownership, quick returns and the codes
+ * of arguments 1-12 as for gemm_f32 (argument 12 is splits here; the stream
+ * is argument 15); -12: splits < 1 or >= 2^31, or s_used*M*N*4 bytes beyond
+ * 2^62; -13: workspace NULL where one is needed; -14: workspace_bytes
+ * smaller than needed.  Runs on the MFMA path. */
+int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
+                    const float *A, int64_t lda,
+                    const float *B, int64_t ldb,
+                    float *C, int64_t ldc,
+                    int transA, int transB, int64_t splits,
+                    float *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace gemm_f32_splitk needs for these sizes: s_used*M*N*4,
+ * or 0 when it runs as a single product.  Negative (-1, -2, -3, -12) for an
+ * invalid M, N, K or splits, numbered as in gemm_f32_splitk. */
+int64_t gemm_f32_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int64_t splits);
+
 /* A static, human-readable description of a return value (never NULL).
- * Messages for -i name gemm_f32's arguments. */
+ * Messages for -1 .. -11 name gemm_f32's arguments; -12 .. -14 list what the
+ * position means for each entry point that uses it. */
 const char *gemm_f32_strerror(int status);
 
 /* Library interface version: major * 10000 + minor * 100 + patch. */

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert g.gemm_f32_version() == 10300
+    assert g.gemm_f32_version() == 10400
 
 
 def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
@@ -134,7 +134,7 @@ def test_operand_layout_from_strides():
 def test_header_is_plain_c():
     """The public header compiles as C with no HIP headers on the include path."""
     import subprocess
-    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10300 ? 0 : 1;}\n"
+    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10400 ? 0 : 1;}\n"
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
                        input=src, capture_output=True, text=True)
@@ -189,3 +189,39 @@ def test_bias_act_invalid_arguments(kwargs, code):
 
 def test_bias_act_quick_return():
     assert g.gemm_f32_bias_act(0, 4, 4, None, 4, FAKE, 4, None, 4, 0, 0, None, 1, None) == 0
+
+
+# ------------------------------------------------------------- split k ---
+
+def splitk(M=8, N=8, K=64, splits=2, ws=FAKE, ws_bytes=1 << 20, **kw):
+    return g.gemm_f32_splitk(M, N, K, kw.get("A", FAKE), kw.get("lda", max(K, 1)),
+                             kw.get("B", FAKE), kw.get("ldb", max(N, 1)), kw.get("C", FAKE),
+                             kw.get("ldc", max(N, 1)), 0, 0,
+                             splits, ws, ws_bytes, None)
+
+
+def test_splitk_workspace_size():
+    """Runs of ceil(K/splits) rounded up to 32; one M x N partial per run."""
+    ws = g.gemm_f32_splitk_workspace_size
+    assert ws(1024, 4096, 8192, 2) == 2 * 1024 * 4096 * 4
+    assert ws(10, 10, 33, 2) == 2 * 10 * 10 * 4      # runs of 32: 32 + 1
+    assert ws(10, 10, 100, 50) == 4 * 10 * 10 * 4    # capped at 32-k runs
+    assert ws(10, 10, 100, 3) == 2 * 10 * 10 * 4     # ceil(100/3) = 34 -> runs of 64: 64 + 36
+    assert ws(10, 10, 32, 4) == 0                    # one run: no workspace
+    assert ws(10, 10, 0, 4) == 0 and ws(0, 10, 64, 2) == 0 and ws(10, 0, 64, 2) == 0
+    assert ws(-1, 1, 1, 1) == -1 and ws(1, -1, 1, 1) == -2 and ws(1, 1, -1, 1) == -3
+    assert ws(1, 1, 1, 0) == -12 and ws(1, 1, 1, -3) == -12
+
+
+def test_splitk_argument_errors():
+    assert splitk(splits=0) == -12
+    assert splitk(ws=None) == -13
+    assert splitk(ws_bytes=2 * 8 * 8 * 4 - 1) == -14
+    assert splitk(M=-1) == -1 and splitk(lda=3) == -5
+    assert "splits" in g.gemm_f32_strerror(-12)
+    assert "workspace" in g.gemm_f32_strerror(-13) and "workspace" in g.gemm_f32_strerror(-14)
+
+
+def test_splitk_quick_return_without_launch():
+    assert splitk(M=0) == 0 and splitk(N=0) == 0
+    assert splitk(M=0, ws=None, ws_bytes=0) == 0
