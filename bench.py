@@ -183,6 +183,132 @@ def copy_probe(mib: int = 1024, reps: int = 5) -> None:
     print(json.dumps({"copy_probe_bytes_read": n * 4, "bytes_written": n * 4, "reps": reps}))
 
 
+# Row-reduction workloads: the causal softmax of one attention layer's scores
+# (8 sequences x 8 heads x 512 queries over 512 keys, head size 64, so scale
+# 1/8) with its gradient, and the normalisation of the transformer set's
+# activations X[8192 x 1024] with its gradient.
+ROW_OPS = {
+    "softmax": dict(rows=8 * 8 * 512, width=512, seed=3000, fn="rows_softmax_f32"),
+    "softmax-bwd": dict(rows=8 * 8 * 512, width=512, seed=3000, fn="rows_softmax_backward_f32"),
+    "normalize": dict(rows=8192, width=1024, seed=2000, fn="rows_normalize_f32"),
+    "normalize-bwd": dict(rows=8192, width=1024, seed=2000, fn="rows_normalize_backward_f32"),
+}
+
+
+def rows_main(args) -> int:
+    """Time one row reduction on its workload: algorithmic bytes (each input
+    read once, the output written once) over the mean launch time, against
+    the HBM roofline."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import gemm_inputs as gi
+    import dense_fp32_matrix_gemm_amd as g
+    from oracle import rows as R
+
+    spec = ROW_OPS[args.rows]
+    rows, width = spec["rows"], spec["width"]
+    g.load()
+    x = gi.stored_matrix(spec["seed"], rows, width, dist="n01")
+    dy = gi.stored_matrix(spec["seed"] + 2, rows, width, dist="n01")
+    scale, eps = 0.125, 1e-5
+    if args.rows == "softmax-bwd":
+        x = R.softmax(x, width, width, scale).astype(np.float32)  # the forward output y
+    dx, ddy = torch.from_numpy(x).cuda(), torch.from_numpy(dy).cuda()
+    out = torch.empty_like(dx)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    calls = {
+        "softmax": lambda: g.rows_softmax_f32(rows, width, width, 1, scale, dx.data_ptr(), width,
+                                              out.data_ptr(), width, s),
+        "softmax-bwd": lambda: g.rows_softmax_backward_f32(rows, width, scale, dx.data_ptr(), width,
+                                                           ddy.data_ptr(), width, out.data_ptr(),
+                                                           width, s),
+        "normalize": lambda: g.rows_normalize_f32(rows, width, eps, dx.data_ptr(), width,
+                                                  out.data_ptr(), width, s),
+        "normalize-bwd": lambda: g.rows_normalize_backward_f32(rows, width, eps, dx.data_ptr(),
+                                                               width, ddy.data_ptr(), width,
+                                                               out.data_ptr(), width, s),
+    }
+    call = calls[args.rows]
+
+    def step():
+        st = call()
+        if st != 0:
+            raise g.GemmError(st)
+
+    op = {"softmax": "softmax", "softmax-bwd": "softmax_backward", "normalize": "normalize",
+          "normalize-bwd": "normalize_backward"}[args.rows]
+    nbytes = R.algorithmic_bytes(op, rows, width)
+    torch.cuda.synchronize()
+    ms = _timed(step, args.steps, args.warmup)
+    value = nbytes / (ms * 1e-3) / 1e9
+
+    # sampled parity: whole rows against the oracle (a row's causal mask
+    # follows its index r: alone, it is a group of width - r % width queries)
+    got = out.cpu().numpy()
+    pick = np.sort(np.random.default_rng(5).choice(rows, 64, replace=False))
+    if op == "softmax":
+        ref = np.stack([R.softmax(x[r:r + 1], width, width - r % width, scale)[0] for r in pick])
+        bound = 1e-5 * ref + 1e-8
+    elif op == "softmax_backward":
+        ref = R.softmax_backward(x[pick], dy[pick], width, scale)
+        S = np.sum(np.abs(dy[pick].astype(np.float64) * x[pick]), axis=1, keepdims=True)
+        bound = 1e-5 * scale * np.abs(x[pick]) * (np.abs(dy[pick]) + S) + 1e-9
+    elif op == "normalize":
+        ref = R.normalize(x[pick], width, eps)
+        bound = 1e-5 * (np.abs(ref) + 1.0)
+    else:
+        ref = R.normalize_backward(x[pick], dy[pick], width, eps)
+        a64, g64 = x[pick].astype(np.float64), dy[pick].astype(np.float64)
+        sigma = np.sqrt(a64.var(axis=1, keepdims=True) + eps)
+        xhat = (a64 - a64.mean(axis=1, keepdims=True)) / sigma
+        bound = 2e-5 * (np.abs(ref) + (np.abs(g64) + np.abs(g64).mean(axis=1, keepdims=True)
+                                       + np.abs(xhat) * np.abs(g64 * xhat).mean(axis=1, keepdims=True))
+                        / sigma) + 1e-9
+    ratio = np.abs(got[pick] - ref) / bound
+    parity = {"rows": int(len(pick)), "max_err_over_bound": float(np.max(ratio)),
+              "ok": bool(np.all(ratio <= 1.0))}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sample = 1024
+        fn = {"softmax": lambda: R.softmax(x[:sample], width, width, scale),
+              "softmax_backward": lambda: R.softmax_backward(x[:sample], dy[:sample], width, scale),
+              "normalize": lambda: R.normalize(x[:sample], width, eps),
+              "normalize_backward": lambda: R.normalize_backward(x[:sample], dy[:sample], width,
+                                                                 eps)}[op]
+        reps, t = 0, 0.0
+        t0 = time.perf_counter()
+        while t < 10.0:
+            fn()
+            reps += 1
+            t = time.perf_counter() - t0
+        cpu = {"value": R.algorithmic_bytes(op, sample, width) * reps / t / 1e9, "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"first {sample} of {rows} rows, {reps} repetitions in {t:.1f} s "
+                         "(numpy float64, one row at a time)"}
+
+    line = {
+        "metric": f"row reduction HBM throughput ({op}, algorithmic bytes / s)",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.rows, "rows": rows, "width": width,
+                   "scale": scale if "softmax" in op else None, "eps": eps if "normalize" in op else None,
+                   "causal": True if op == "softmax" else None, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": value, "peak": MI355X_HBM_TBPS * 1000,
+                     "unit": "GB/s", "frac": value / (MI355X_HBM_TBPS * 1000), "traffic": None,
+                     "kernel": spec["fn"], "bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "library": os.path.relpath(g.library_path(), ROOT),
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +326,8 @@ def main(argv=None) -> int:
                     help="time the fused C = act(A.B + bias) entry point instead")
     ap.add_argument("--splitk", type=int, default=0,
                     help="time gemm_f32_splitk with this many runs of k (partials plus their sum)")
+    ap.add_argument("--rows", default=None, choices=sorted(ROW_OPS),
+                    help="time a row reduction (GB/s against the HBM roofline) instead of a GEMM")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -217,6 +345,8 @@ def main(argv=None) -> int:
     if args.copy_probe:
         copy_probe()
         return 0
+    if args.rows:
+        return rows_main(args)
 
     torch.backends.cuda.matmul.allow_tf32 = False
     name = args.workload or gi.HEADLINE

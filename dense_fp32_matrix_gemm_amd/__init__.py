@@ -14,14 +14,17 @@ from ._lib import (ACT_GELU, ACT_NONE, ALGOS, LibraryNotBuilt, gemm_f32, gemm_f3
                    gemm_f32_bias_act,
                    gemm_f32_ex, gemm_f32_naive, gemm_f32_splitk, gemm_f32_splitk_workspace_size,
                    gemm_f32_strerror, gemm_f32_strided_batched, gemm_f32_version, library_path,
-                   load)
+                   load, rows_normalize_backward_f32, rows_normalize_f32,
+                   rows_softmax_backward_f32, rows_softmax_f32)
 
 __all__ = ["ACT_GELU", "ACT_NONE", "ALGOS", "GemmError", "LibraryNotBuilt", "bmm", "gemm_f32",
            "gemm_f32_bf16", "gemm_f32_bias_act", "gemm_f32_ex", "linear",
            "gemm_f32_naive", "gemm_f32_splitk", "gemm_f32_splitk_workspace_size",
            "gemm_f32_strerror", "gemm_f32_strided_batched",
            "gemm_f32_version", "library_path", "load", "matmul", "matmul_splitk",
-           "operand_layout"]
+           "normalize", "normalize_backward", "operand_layout", "rows_normalize_backward_f32",
+           "rows_normalize_f32", "rows_softmax_backward_f32", "rows_softmax_f32", "softmax",
+           "softmax_backward"]
 
 
 class GemmError(RuntimeError):
@@ -180,6 +183,73 @@ def matmul_splitk(a, b, splits: int, out=None, workspace=None, stream=None):
         stream = torch.cuda.current_stream(a.device).cuda_stream
     st = gemm_f32_splitk(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
                          ta, tb, splits, ws_ptr, ws_bytes, stream)
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+# ------------------------------------------------------------ row operations ---
+
+def _row_major(t, name):
+    import torch
+    if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D float32 device tensor")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return max(t.stride(0), cols, 1) if rows > 1 else max(cols, 1)
+
+
+def _out_like(x, out):
+    import torch
+    return torch.empty_like(x, memory_format=torch.contiguous_format) if out is None else out
+
+
+def _stream(x, stream):
+    import torch
+    return torch.cuda.current_stream(x.device).cuda_stream if stream is None else stream
+
+
+def softmax(x, scale: float = 1.0, queries=None, causal: bool = True, out=None, stream=None):
+    """Softmax of scale * x along rows; causal: rows are groups of ``queries``
+    query rows (default: the row length) masking the future (rows_softmax_f32)."""
+    rows, width = x.shape
+    out = _out_like(x, out)
+    q = width if queries is None else queries
+    st = rows_softmax_f32(rows, width, q, int(causal), scale, x.data_ptr(), _row_major(x, "x"),
+                          out.data_ptr(), _row_major(out, "out"), _stream(x, stream))
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def softmax_backward(y, dy, scale: float = 1.0, out=None, stream=None):
+    rows, width = y.shape
+    out = _out_like(y, out)
+    st = rows_softmax_backward_f32(rows, width, scale, y.data_ptr(), _row_major(y, "y"),
+                                   dy.data_ptr(), _row_major(dy, "dy"), out.data_ptr(),
+                                   _row_major(out, "out"), _stream(y, stream))
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def normalize(x, eps: float = 1e-5, out=None, stream=None):
+    rows, n = x.shape
+    out = _out_like(x, out)
+    st = rows_normalize_f32(rows, n, eps, x.data_ptr(), _row_major(x, "x"), out.data_ptr(),
+                            _row_major(out, "out"), _stream(x, stream))
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def normalize_backward(x, dy, eps: float = 1e-5, out=None, stream=None):
+    rows, n = x.shape
+    out = _out_like(x, out)
+    st = rows_normalize_backward_f32(rows, n, eps, x.data_ptr(), _row_major(x, "x"),
+                                     dy.data_ptr(), _row_major(dy, "dy"), out.data_ptr(),
+                                     _row_major(out, "out"), _stream(x, stream))
     if st != 0:
         raise GemmError(st)
     return out

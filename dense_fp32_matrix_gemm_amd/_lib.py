@@ -1,4 +1,5 @@
-"""ctypes binding of ``libgemm_f32.so`` (declarations: include/gemm_f32.h).
+"""ctypes binding of ``libgemm_f32.so`` (declarations: include/gemm_f32.h and
+include/rows_f32.h).
 
 Argument marshalling only: every step of the product runs in the library's
 HIP kernels.  Loading fails loudly if the library has not been built; there
@@ -20,7 +21,7 @@ ALGOS = {"auto": ALGO_AUTO, "mfma": ALGO_MFMA, "fma": ALGO_FMA, "tiled": ALGO_TI
          "mfma256": ALGO_MFMA_TILE256}
 
 # Every symbol include/gemm_f32.h declares, with (restype, argtypes).
-_i64, _ptr, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+_i64, _ptr, _int, _flt = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 _GEMM_ARGS = [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int, _ptr]
 SIGNATURES = {
     "gemm_f32": (_int, _GEMM_ARGS),
@@ -35,6 +36,11 @@ SIGNATURES = {
                                _i64, _ptr, _i64, _ptr]),
     "gemm_f32_splitk_workspace_size": (_i64, [_i64, _i64, _i64, _i64]),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
+    "rows_softmax_f32": (_int, [_i64, _i64, _i64, _int, _flt, _ptr, _i64, _ptr, _i64, _ptr]),
+    "rows_softmax_backward_f32": (_int, [_i64, _i64, _flt, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr]),
+    "rows_normalize_f32": (_int, [_i64, _i64, _flt, _ptr, _i64, _ptr, _i64, _ptr]),
+    "rows_normalize_backward_f32": (_int, [_i64, _i64, _flt, _ptr, _i64, _ptr, _i64, _ptr, _i64,
+                                           _ptr]),
     "gemm_f32_version": (_int, []),
 }
 
@@ -116,6 +122,24 @@ def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, splits, wor
 
 def gemm_f32_splitk_workspace_size(M, N, K, splits) -> int:
     return int(load().gemm_f32_splitk_workspace_size(M, N, K, splits))
+
+
+def rows_softmax_f32(rows, width, queries, causal, scale, x, ldx, y, ldy, stream) -> int:
+    """Causal (or plain) softmax of scale * x along each row (include/rows_f32.h)."""
+    return _call("rows_softmax_f32", rows, width, queries, causal, scale, x, ldx, y, ldy, stream)
+
+
+def rows_softmax_backward_f32(rows, width, scale, y, ldy, dy, lddy, dx, lddx, stream) -> int:
+    return _call("rows_softmax_backward_f32", rows, width, scale, y, ldy, dy, lddy, dx, lddx,
+                 stream)
+
+
+def rows_normalize_f32(rows, n, eps, x, ldx, y, ldy, stream) -> int:
+    return _call("rows_normalize_f32", rows, n, eps, x, ldx, y, ldy, stream)
+
+
+def rows_normalize_backward_f32(rows, n, eps, x, ldx, dy, lddy, dx, lddx, stream) -> int:
+    return _call("rows_normalize_backward_f32", rows, n, eps, x, ldx, dy, lddy, dx, lddx, stream)
 
 
 def gemm_f32_strerror(status: int) -> str:

@@ -225,3 +225,37 @@ def test_splitk_argument_errors():
 def test_splitk_quick_return_without_launch():
     assert splitk(M=0) == 0 and splitk(N=0) == 0
     assert splitk(M=0, ws=None, ws_bytes=0) == 0
+
+
+# --------------------------------------------------------- row reductions ---
+
+def test_rows_header_is_plain_c():
+    import subprocess
+    src = "#include \"rows_f32.h\"\nint main(void){return 0;}\n"
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_rows_argument_errors():
+    sm = lambda **k: g.rows_softmax_f32(k.get("rows", 4), k.get("width", 8), k.get("q", 8),
+                                        k.get("causal", 1), 1.0, k.get("x", FAKE),
+                                        k.get("ldx", 8), k.get("y", FAKE), k.get("ldy", 8), None)
+    assert sm(rows=-1) == -1 and sm(width=-1) == -2 and sm(width=BIG) == -2
+    assert sm(q=0) == -3 and sm(q=9) == -3 and sm(causal=2) == -4
+    assert sm(x=None) == -6 and sm(ldx=7) == -7 and sm(y=None) == -8 and sm(ldy=0) == -9
+    assert sm(rows=0) == 0 and sm(width=0, ldx=1, ldy=1, q=5) == 0   # nothing to do, no launch
+    sb = lambda **k: g.rows_softmax_backward_f32(4, k.get("width", 8), 1.0, k.get("y", FAKE), 8,
+                                                 k.get("dy", FAKE), k.get("lddy", 8),
+                                                 k.get("dx", FAKE), 8, None)
+    assert sb(y=None) == -4 and sb(dy=None) == -6 and sb(lddy=3) == -7 and sb(dx=None) == -8
+    nm = lambda **k: g.rows_normalize_f32(k.get("rows", 4), 8, k.get("eps", 1e-5),
+                                          k.get("x", FAKE), 8, k.get("y", FAKE), k.get("ldy", 8),
+                                          None)
+    assert nm(eps=-1.0) == -3 and nm(eps=float("nan")) == -3 and nm(eps=float("inf")) == -3
+    assert nm(x=None) == -4 and nm(y=None) == -6 and nm(ldy=2) == -7 and nm(rows=0) == 0
+    nb = lambda **k: g.rows_normalize_backward_f32(4, 8, 1e-5, k.get("x", FAKE), 8,
+                                                   k.get("dy", FAKE), 8, k.get("dx", FAKE),
+                                                   k.get("lddx", 8), None)
+    assert nb(x=None) == -4 and nb(dy=None) == -6 and nb(dx=None) == -8 and nb(lddx=1) == -9
