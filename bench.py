@@ -77,6 +77,7 @@ KERNEL_SOURCES = {
     "gemm_f32_tiled": ["gemm_simple.hip", "gemm_internal.hpp"],
     "gemm_f32_naive": ["gemm_simple.hip", "gemm_internal.hpp"],
     "gemm_f32_bf16": ["gemm_bf16.hip", "tile_common.hpp", "gemm_internal.hpp"],
+    "rows_softmax_f32": ["rows.hip", "gemm_internal.hpp", "../../include/rows_f32.h"],
 }
 
 
@@ -298,7 +299,8 @@ def rows_main(args) -> int:
                    "scale": scale if "softmax" in op else None, "eps": eps if "normalize" in op else None,
                    "causal": True if op == "softmax" else None, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": value, "peak": MI355X_HBM_TBPS * 1000,
-                     "unit": "GB/s", "frac": value / (MI355X_HBM_TBPS * 1000), "traffic": None,
+                     "unit": "GB/s", "frac": value / (MI355X_HBM_TBPS * 1000),
+                     "traffic": read_traffic(spec["fn"], args.rows),
                      "kernel": spec["fn"], "bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
         "parity": parity,

@@ -35,7 +35,8 @@ extern "C" {
  *     y[r][c] = exp(scale*x[r][c] - m_r - log s_r)   for kept columns,
  *     y[r][c] = 0                                      otherwise,
  * m_r the maximum of scale*x over row r's kept columns and s_r the sum over
- * them of exp(scale*x - m_r).  causal = 1: rows come in groups of `queries`
+ * them of exp(scale*x - m_r) (computed as exp(scale*x - m_r) / s_r, the same
+ * value, with one exponential per element).  causal = 1: rows come in groups of `queries`
  * consecutive query rows (one group per sequence and head) whose queries are
  * the last `queries` of `width` positions, so row r's query is at position
  * width - queries + r % queries and the kept columns are those at or before
