@@ -36,8 +36,16 @@ def sources() -> List[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, verbose: bool, extra: List[str]) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+# Evidence builds: the same sources with one design choice undone, written
+# next to the library under their own names (load one with the environment
+# variable GEMM_F32_LIBRARY).  Not used by the package itself.
+ABLATIONS = {
+    "noswizzle": ["-DGEMM_MFMA_SWIZZLE=0"],  # MFMA kernel LDS rows without the XOR swizzle
+}
+
+
+def _compile(src: str, verbose: bool, extra: List[str], build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *COMMON, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -53,17 +61,24 @@ def _compile(src: str, verbose: bool, extra: List[str]) -> str:
 
 
 def build(verbose: bool = False, output: Optional[str] = None,
-          extra_flags: Optional[List[str]] = None, jobs: Optional[int] = None) -> str:
-    """Compile and link the library; returns the path of the ``.so``."""
-    output = output or LIBRARY
+          extra_flags: Optional[List[str]] = None, jobs: Optional[int] = None,
+          ablation: Optional[str] = None) -> str:
+    """Compile and link the library (or one of the ABLATIONS, as
+    libgemm_f32_<name>.so); returns the path of the ``.so``."""
     extra = list(extra_flags or [])
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    build_dir = BUILD_DIR
+    if ablation is not None:
+        extra += ABLATIONS[ablation]
+        build_dir = os.path.join(BUILD_DIR, ablation)
+        output = output or os.path.join(PKG, f"libgemm_f32_{ablation}.so")
+    output = output or LIBRARY
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     if not srcs:
         raise RuntimeError(f"no HIP sources under {CSRC}")
     jobs = jobs or min(len(srcs), 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, extra), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, extra, build_dir), srcs))
     tmp = output + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
@@ -76,4 +91,5 @@ def build(verbose: bool = False, output: Optional[str] = None,
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    abl = sys.argv[sys.argv.index("--ablation") + 1] if "--ablation" in sys.argv else None
+    print(build(verbose="-v" in sys.argv, ablation=abl))

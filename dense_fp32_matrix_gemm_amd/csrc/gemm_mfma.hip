@@ -125,6 +125,13 @@ struct Config {
                   "a k-slice's partial tile fits in one stage buffer for the reduction");
 };
 
+// GEMM_MFMA_SWIZZLE 0 builds the ablation with unswizzled LDS rows (the same
+// results; its bank conflicts show what the swizzle removes).  The library
+// is built with 1.
+#ifndef GEMM_MFMA_SWIZZLE
+#define GEMM_MFMA_SWIZZLE 1
+#endif
+
 // LDS tile of one operand for one stage.  P = extent along m (or n); KC =
 // the stored rows of the operand run along k (A untransposed, B transposed):
 // then the tile is P rows of BK floats, else BK rows of P floats.  Rows are
@@ -165,6 +172,7 @@ struct Tile {
     //   ((r >> 1) ^ (r >> 2)) & 3.
     __device__ static __forceinline__ int swz(int r)
     {
+        if (!GEMM_MFMA_SWIZZLE) return 0;  // the unswizzled ablation build
         if (KC) {
             if (vpr == 4) return ((r >> 1) ^ (r >> 2)) & 3;
             return ((r & 7) ^ ((r >> 3) & 1)) & (vpr - 1);
