@@ -41,6 +41,7 @@ def sources() -> List[str]:
 # variable GEMM_F32_LIBRARY).  Not used by the package itself.
 ABLATIONS = {
     "noswizzle": ["-DGEMM_MFMA_SWIZZLE=0"],  # MFMA kernel LDS rows without the XOR swizzle
+    "nopad": ["-DGEMM_FMA_PAD=0"],           # vector-FMA kernel LDS rows without padding
 }
 
 

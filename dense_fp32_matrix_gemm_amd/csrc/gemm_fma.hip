@@ -27,7 +27,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int TM = 8, TN = 8;
-constexpr int kPad = 4;
+// Row padding of the LDS tiles (section 3.6's remedy for bank conflicts);
+// GEMM_FMA_PAD 0 builds the unpadded ablation (same results).
+#ifndef GEMM_FMA_PAD
+#define GEMM_FMA_PAD 4
+#endif
+constexpr int kPad = GEMM_FMA_PAD;
 constexpr int kLd = 128 + kPad;  // LDS row length, both operands (BM == BN)
 constexpr int kGroupM = 8;
 
