@@ -1,11 +1,14 @@
 """FP32 dense GEMM for AMD Instinct MI355X (gfx950).
 
 The product runs in hand-written HIP kernels behind a C ABI
-(``include/gemm_f32.h``, library ``libgemm_f32.so``).  This package is the
-thin Python side: the raw ABI calls (``gemm_f32``, ``gemm_f32_naive``,
-``gemm_f32_ex``, ``gemm_f32_strerror``, ``gemm_f32_version``) and ``matmul``,
-which takes PyTorch device tensors, reads their pointers, strides and the
-current stream, and calls the library.  PyTorch owns memory and streams.
+(``include/gemm_f32.h`` and ``include/rows_f32.h``, library
+``libgemm_f32.so``).  This package is the thin Python side: the raw ABI
+calls under their C names, and tensor-level helpers (``matmul``, ``bmm``,
+``linear``, ``matmul_splitk``, ``softmax``, ``softmax_backward``,
+``normalize``, ``normalize_backward``) that take PyTorch device tensors,
+read their pointers, strides and the current stream, and call the library.
+PyTorch owns memory and streams; every step of the computation runs in the
+library's kernels.
 """
 
 from __future__ import annotations

@@ -255,3 +255,31 @@ def test_rows_repeatable():
             first = got
         for a, b in zip(first, got):
             assert np.array_equal(a, b)
+
+
+def test_tensor_helpers_match_the_oracle():
+    """The tensor-level wrappers (softmax, softmax_backward, normalize,
+    normalize_backward) on padded views, against the oracle."""
+    import torch
+    import dense_fp32_matrix_gemm_amd as g
+    rows, width = 96, 200
+    x = stored(21, rows, width, width + 4)
+    dy = stored(22, rows, width, width + 4)
+    dx_t, ddy_t = P.to_device(x)[:, :width], P.to_device(dy)[:, :width]
+    y = g.softmax(dx_t, 0.5, queries=8)
+    g_soft = g.softmax_backward(y, ddy_t, 0.5)
+    n = g.normalize(dx_t, 1e-4)
+    g_norm = g.normalize_backward(dx_t, ddy_t, 1e-4)
+    torch.cuda.synchronize()
+    ref_y = R.softmax(x, width, 8, 0.5)
+    check_softmax(np.concatenate([y.cpu().numpy(), np.full((rows, 1), PAD, np.float32)], 1),
+                  ref_y, width)
+    y32 = y.cpu().numpy()
+    ref = R.softmax_backward(y32, dy, width, 0.5)
+    S = np.sum(np.abs(dy[:, :width].astype(np.float64) * y32), axis=1, keepdims=True)
+    assert np.all(np.abs(g_soft.cpu().numpy() - ref)
+                  <= 1e-5 * 0.5 * np.abs(y32) * (np.abs(dy[:, :width]) + S) + 1e-9)
+    refn = R.normalize(x, width, 1e-4)
+    assert np.all(np.abs(n.cpu().numpy() - refn) <= norm_bound(refn))
+    refb = R.normalize_backward(x, dy, width, 1e-4)
+    assert np.all(np.abs(g_norm.cpu().numpy() - refb) <= 1e-4 * (np.abs(refb) + 1.0))
