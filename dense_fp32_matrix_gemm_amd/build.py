@@ -42,6 +42,7 @@ def sources() -> List[str]:
 ABLATIONS = {
     "noswizzle": ["-DGEMM_MFMA_SWIZZLE=0"],  # MFMA kernel LDS rows without the XOR swizzle
     "nopad": ["-DGEMM_FMA_PAD=0"],           # vector-FMA kernel LDS rows without padding
+    "singlebuffer": ["-DGEMM_MFMA_SINGLE_BUFFER=1"],  # MFMA kernel: copy/barrier/compute/barrier
 }
 
 

@@ -125,6 +125,13 @@ struct Config {
                   "a k-slice's partial tile fits in one stage buffer for the reduction");
 };
 
+// GEMM_MFMA_SINGLE_BUFFER 1 builds the ablation without double buffering:
+// one stage buffer, each copy issued after the previous stage's compute and
+// awaited before the next (the same results).
+#ifndef GEMM_MFMA_SINGLE_BUFFER
+#define GEMM_MFMA_SINGLE_BUFFER 0
+#endif
+
 // GEMM_MFMA_SWIZZLE 0 builds the ablation with unswizzled LDS rows (the same
 // results; its bank conflicts show what the swizzle removes).  The library
 // is built with 1.
@@ -419,8 +426,8 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             TB::dma(lds + TA::floats, gb + stage * b_step, ob, wave);
         };
         dma(buf0, 0);
-        if (NB > 2 && 1 < full) dma(bufp(Int<1 % NB>{}), 1);
-        if (NB > 3 && 2 < full) dma(bufp(Int<2 % NB>{}), 2);
+        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 2 && 1 < full) dma(bufp(Int<1 % NB>{}), 1);
+        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 3 && 2 < full) dma(bufp(Int<2 % NB>{}), 2);
         // TRIP stages per trip (a multiple of NB and of FOLD) so that each
         // buffer and each chunk boundary is a compile-time choice.
         constexpr int TRIP = NB > FOLD ? NB : FOLD;
@@ -428,7 +435,15 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             unroll_for<TRIP>([&](auto bi) {
                 constexpr int b = decltype(bi)::value;
                 const int st = s + b;
-                if (st < full) {
+                if (GEMM_MFMA_SINGLE_BUFFER && st < full) {
+                    // The ablation: the course page's pattern with one
+                    // buffer -- copy, barrier, compute, barrier, next copy.
+                    wait_vm<0>();
+                    __syncthreads();
+                    compute(buf0, nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{});
+                    __syncthreads();
+                    if (st + 1 < full) dma(buf0, st + 1);
+                } else if (st < full) {
                     // Stage st has landed (at most the copies of the NB - 2
                     // later stages are outstanding); after the barrier every
                     // wave's share is visible, and every wave is done with
