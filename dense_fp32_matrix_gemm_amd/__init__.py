@@ -36,6 +36,20 @@ class GemmError(RuntimeError):
         super().__init__(f"gemm_f32 status {status}: {gemm_f32_strerror(status)}")
 
 
+def _check_tensor(t, name, device=None, dims=2):
+    """A float32 tensor on the GPU (and on ``device`` if given): the library
+    dereferences its pointer on the device, so anything else is refused here."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+        raise TypeError(f"{name} must be a float32 tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the operands on {device}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must be {dims}-D")
+
+
 def operand_layout(t) -> tuple:
     """(trans, ld) describing a 2-D tensor view for the row-major ABI.
 
@@ -63,17 +77,16 @@ def matmul(a, b, out=None, algo: str = "auto", stream=None):
     """
     import torch
 
-    if a.dtype != torch.float32 or b.dtype != torch.float32:
-        raise TypeError("matmul takes float32 tensors")
-    if not (a.is_cuda and b.is_cuda):
-        raise ValueError("matmul takes device tensors")
+    _check_tensor(a, "a")
+    _check_tensor(b, "b", a.device)
     M, K = a.shape
     K2, N = b.shape
     if K2 != K:
         raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=a.device)
-    if out.shape != (M, N) or out.dtype != torch.float32 or (N > 1 and out.stride(1) != 1):
+    _check_tensor(out, "out", a.device)
+    if out.shape != (M, N) or (N > 1 and out.stride(1) != 1):
         raise ValueError("out must be an M x N float32 tensor with unit column stride")
     ta, lda = operand_layout(a)
     tb, ldb = operand_layout(b)
@@ -97,16 +110,15 @@ def bmm(a, b, out=None, stream=None):
     """
     import torch
 
-    if a.dim() != 3 or b.dim() != 3:
-        raise ValueError("bmm operands are 3-D")
-    if a.dtype != torch.float32 or b.dtype != torch.float32:
-        raise TypeError("bmm takes float32 tensors")
+    _check_tensor(a, "a", dims=3)
+    _check_tensor(b, "b", a.device, dims=3)
     batch, M, K = a.shape
     if b.shape[0] != batch or b.shape[1] != K:
         raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not chain")
     N = b.shape[2]
     if out is None:
         out = torch.empty((batch, M, N), dtype=torch.float32, device=a.device)
+    _check_tensor(out, "out", a.device, dims=3)
     if out.shape != (batch, M, N) or (N > 1 and out.stride(2) != 1):
         raise ValueError("out must be (batch, M, N) with unit column stride")
     ta, lda = operand_layout(a[0]) if batch else (0, max(K, 1))
@@ -130,18 +142,22 @@ def linear(x, w, bias=None, activation=None, out=None, stream=None):
     """
     import torch
 
-    if x.dtype != torch.float32 or w.dtype != torch.float32:
-        raise TypeError("linear takes float32 tensors")
+    _check_tensor(x, "x")
+    _check_tensor(w, "w", x.device)
     M, K = x.shape
     K2, N = w.shape
     if K2 != K:
         raise ValueError(f"inner dimensions differ: {tuple(x.shape)} @ {tuple(w.shape)}")
     act = {None: ACT_NONE, "gelu": ACT_GELU}[activation]
-    if bias is not None and (bias.shape != (N,) or bias.dtype != torch.float32 or
-                             (N > 1 and bias.stride(0) != 1)):
-        raise ValueError("bias must be a contiguous float32 vector of N entries")
+    if bias is not None:
+        _check_tensor(bias, "bias", x.device, dims=1)
+        if bias.shape != (N,) or (N > 1 and bias.stride(0) != 1):
+            raise ValueError("bias must be a contiguous float32 vector of N entries")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_tensor(out, "out", x.device)
+    if out.shape != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be an M x N float32 tensor with unit column stride")
     ta, lda = operand_layout(x)
     tb, ldb = operand_layout(w)
     ldc = max(out.stride(0), N, 1) if M > 1 else max(N, 1)
@@ -160,23 +176,24 @@ def matmul_splitk(a, b, splits: int, out=None, workspace=None, stream=None):
     gemm_f32_splitk_workspace_size bytes; if None one is allocated here."""
     import torch
 
-    if a.dtype != torch.float32 or b.dtype != torch.float32:
-        raise TypeError("matmul_splitk takes float32 tensors")
-    if not (a.is_cuda and b.is_cuda):
-        raise ValueError("matmul_splitk takes device tensors")
+    _check_tensor(a, "a")
+    _check_tensor(b, "b", a.device)
     M, K = a.shape
     K2, N = b.shape
     if K2 != K:
         raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=a.device)
-    if out.shape != (M, N) or out.dtype != torch.float32 or (N > 1 and out.stride(1) != 1):
+    _check_tensor(out, "out", a.device)
+    if out.shape != (M, N) or (N > 1 and out.stride(1) != 1):
         raise ValueError("out must be an M x N float32 tensor with unit column stride")
     need = gemm_f32_splitk_workspace_size(M, N, K, splits)
     if need < 0:
         raise GemmError(int(need))
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=a.device)
+    if workspace is not None:
+        _check_tensor(workspace, "workspace", a.device, dims=workspace.dim())
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ta, lda = operand_layout(a)
@@ -193,10 +210,12 @@ def matmul_splitk(a, b, splits: int, out=None, workspace=None, stream=None):
 
 # ------------------------------------------------------------ row operations ---
 
-def _row_major(t, name):
-    import torch
-    if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2:
-        raise TypeError(f"{name} must be a 2-D float32 device tensor")
+def _row_major(t, name, like=None):
+    """Leading dimension of a 2-D row-major device tensor; ``like``: a tensor
+    it must match in shape and device."""
+    _check_tensor(t, name, None if like is None else like.device)
+    if like is not None and t.shape != like.shape:
+        raise ValueError(f"{name} must have shape {tuple(like.shape)}, not {tuple(t.shape)}")
     rows, cols = t.shape
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit column stride")
@@ -220,7 +239,7 @@ def softmax(x, scale: float = 1.0, queries=None, causal: bool = True, out=None, 
     out = _out_like(x, out)
     q = width if queries is None else queries
     st = rows_softmax_f32(rows, width, q, int(causal), scale, x.data_ptr(), _row_major(x, "x"),
-                          out.data_ptr(), _row_major(out, "out"), _stream(x, stream))
+                          out.data_ptr(), _row_major(out, "out", x), _stream(x, stream))
     if st != 0:
         raise GemmError(st)
     return out
@@ -230,8 +249,8 @@ def softmax_backward(y, dy, scale: float = 1.0, out=None, stream=None):
     rows, width = y.shape
     out = _out_like(y, out)
     st = rows_softmax_backward_f32(rows, width, scale, y.data_ptr(), _row_major(y, "y"),
-                                   dy.data_ptr(), _row_major(dy, "dy"), out.data_ptr(),
-                                   _row_major(out, "out"), _stream(y, stream))
+                                   dy.data_ptr(), _row_major(dy, "dy", y), out.data_ptr(),
+                                   _row_major(out, "out", y), _stream(y, stream))
     if st != 0:
         raise GemmError(st)
     return out
@@ -241,7 +260,7 @@ def normalize(x, eps: float = 1e-5, out=None, stream=None):
     rows, n = x.shape
     out = _out_like(x, out)
     st = rows_normalize_f32(rows, n, eps, x.data_ptr(), _row_major(x, "x"), out.data_ptr(),
-                            _row_major(out, "out"), _stream(x, stream))
+                            _row_major(out, "out", x), _stream(x, stream))
     if st != 0:
         raise GemmError(st)
     return out
@@ -251,8 +270,8 @@ def normalize_backward(x, dy, eps: float = 1e-5, out=None, stream=None):
     rows, n = x.shape
     out = _out_like(x, out)
     st = rows_normalize_backward_f32(rows, n, eps, x.data_ptr(), _row_major(x, "x"),
-                                     dy.data_ptr(), _row_major(dy, "dy"), out.data_ptr(),
-                                     _row_major(out, "out"), _stream(x, stream))
+                                     dy.data_ptr(), _row_major(dy, "dy", x), out.data_ptr(),
+                                     _row_major(out, "out", x), _stream(x, stream))
     if st != 0:
         raise GemmError(st)
     return out

@@ -259,3 +259,17 @@ def test_rows_argument_errors():
                                                    k.get("dy", FAKE), 8, k.get("dx", FAKE),
                                                    k.get("lddx", 8), None)
     assert nb(x=None) == -4 and nb(dy=None) == -6 and nb(dx=None) == -8 and nb(lddx=1) == -9
+
+
+def test_tensor_helpers_refuse_host_tensors():
+    """The tensor-level helpers check dtype and device before any library
+    call: a host tensor's pointer must never reach a kernel."""
+    import torch
+    x = torch.ones(4, 4)
+    for call in (lambda: g.matmul(x, x), lambda: g.linear(x, x), lambda: g.matmul_splitk(x, x, 2),
+                 lambda: g.bmm(x[None], x[None]), lambda: g.softmax(x), lambda: g.normalize(x),
+                 lambda: g.softmax_backward(x, x), lambda: g.normalize_backward(x, x)):
+        with pytest.raises(ValueError, match="device tensor"):
+            call()
+    with pytest.raises(TypeError, match="float32"):
+        g.matmul(x.double(), x.double())

@@ -283,3 +283,13 @@ def test_tensor_helpers_match_the_oracle():
     assert np.all(np.abs(n.cpu().numpy() - refn) <= norm_bound(refn))
     refb = R.normalize_backward(x, dy, width, 1e-4)
     assert np.all(np.abs(g_norm.cpu().numpy() - refb) <= 1e-4 * (np.abs(refb) + 1.0))
+
+
+def test_tensor_helpers_refuse_mismatched_shapes():
+    import dense_fp32_matrix_gemm_amd as g
+    x = P.to_device(stored(23, 16, 32, 32))
+    small = P.to_device(stored(24, 8, 32, 32))
+    for call in (lambda: g.softmax(x, out=small), lambda: g.normalize(x, out=small),
+                 lambda: g.softmax_backward(x, small), lambda: g.normalize_backward(x, small)):
+        with pytest.raises(ValueError, match="shape"):
+            call()
