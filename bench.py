@@ -19,6 +19,9 @@ Besides the metric the line carries:
                 inputs, for comparison;
   parity        a sampled check of the timed result against the oracle.
 
+cpu_baseline and parity form the CPU-baseline leg, the only part of this
+script that runs the oracle (skipped with --no-cpu-baseline).
+
 ``--algo bf16`` times the mixed-precision entry point instead (operands
 rounded to bf16, FP32 sums) against the dense bf16 matrix peak (2.5 PFLOP/s).
 
@@ -143,6 +146,30 @@ def _lscpu_model() -> str:
     return "unknown"
 
 
+def sampled_parity(w, A, B, c_host, mixed: bool, bias, act: int) -> dict:
+    """Part of the CPU-baseline leg: 256 sampled entries of the timed result
+    (the last product of a batch) against the oracle, to the FP32 bar."""
+    import numpy as np
+    import gemm_inputs as gi
+    import oracle
+    orc = oracle.load()
+    rows, cols = gi.sample_entries(w.M, w.N, 256, seed=23)
+    a0, b0, c0 = A, B, c_host
+    if w.batch > 1:
+        last = w.batch - 1
+        a0 = A[last, :w.a_dims[0] * w.lda_].reshape(w.a_dims[0], w.lda_)
+        b0 = B if w.shared_b else B[last, :w.b_dims[0] * w.ldb_].reshape(w.b_dims[0], w.ldb_)
+        c0 = c0[last, :w.M * w.ldc_].reshape(w.M, w.ldc_)
+    entries = orc.entries_bf16 if mixed else orc.entries
+    ref = entries(a0, b0, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
+    if bias is not None:
+        ref = orc.epilogue((ref + bias[cols].astype(np.float64))[None, :], None, act)[0]
+    got = c0[rows, cols].astype(np.float64)
+    ratio = np.abs(got - ref) / (1e-6 * w.K + 1e-5 * np.abs(ref))
+    return {"entries": int(rows.size), "max_err_over_bound": float(np.max(ratio)),
+            "ok": bool(np.all(ratio <= 1.0))}
+
+
 def cpu_baseline(w, target_s: float = 12.0, mixed: bool = False) -> dict:
     """The oracle, as it stands, on a row panel of the workload's product
     (its mixed-precision function when ``mixed``)."""
@@ -196,6 +223,62 @@ ROW_OPS = {
 }
 
 
+def row_bytes(op: str, rows: int, width: int) -> int:
+    """Algorithmic bytes of a row reduction: each input read once and the
+    output written once, 4 bytes per element (one input for the forward
+    passes, two for the gradients)."""
+    inputs = 2 if op.endswith("backward") else 1
+    return 4 * (inputs + 1) * rows * width
+
+
+def rows_oracle_leg(op, x, dy, got, rows, width, scale, eps):
+    """The CPU-baseline leg of a row-reduction run, the only place it runs
+    the oracle: 64 sampled rows of the timed result against it, and the
+    oracle itself timed on the first 1024 rows (about 10 s, one core)."""
+    import numpy as np
+    from oracle import rows as R
+    pick = np.sort(np.random.default_rng(5).choice(rows, 64, replace=False))
+    if op == "softmax":
+        # a row's causal mask follows its index r: alone, it is a group of
+        # width - r % width queries
+        ref = np.stack([R.softmax(x[r:r + 1], width, width - r % width, scale)[0] for r in pick])
+        bound = 1e-5 * ref + 1e-8
+    elif op == "softmax_backward":
+        ref = R.softmax_backward(x[pick], dy[pick], width, scale)
+        S = np.sum(np.abs(dy[pick].astype(np.float64) * x[pick]), axis=1, keepdims=True)
+        bound = 1e-5 * scale * np.abs(x[pick]) * (np.abs(dy[pick]) + S) + 1e-9
+    elif op == "normalize":
+        ref = R.normalize(x[pick], width, eps)
+        bound = 1e-5 * (np.abs(ref) + 1.0)
+    else:
+        ref = R.normalize_backward(x[pick], dy[pick], width, eps)
+        a64, g64 = x[pick].astype(np.float64), dy[pick].astype(np.float64)
+        sigma = np.sqrt(a64.var(axis=1, keepdims=True) + eps)
+        xhat = (a64 - a64.mean(axis=1, keepdims=True)) / sigma
+        bound = 2e-5 * (np.abs(ref) + (np.abs(g64) + np.abs(g64).mean(axis=1, keepdims=True)
+                                       + np.abs(xhat) * np.abs(g64 * xhat).mean(axis=1, keepdims=True))
+                        / sigma) + 1e-9
+    ratio = np.abs(got[pick] - ref) / bound
+    parity = {"rows": int(len(pick)), "max_err_over_bound": float(np.max(ratio)),
+              "ok": bool(np.all(ratio <= 1.0))}
+    sample = 1024
+    fn = {"softmax": lambda: R.softmax(x[:sample], width, width, scale),
+          "softmax_backward": lambda: R.softmax_backward(x[:sample], dy[:sample], width, scale),
+          "normalize": lambda: R.normalize(x[:sample], width, eps),
+          "normalize_backward": lambda: R.normalize_backward(x[:sample], dy[:sample], width, eps)}[op]
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while t < 10.0:
+        fn()
+        reps += 1
+        t = time.perf_counter() - t0
+    cpu = {"value": row_bytes(op, sample, width) * reps / t / 1e9, "unit": "GB/s",
+           "cores": 1, "kind": "oracle",
+           "sample": f"first {sample} of {rows} rows, {reps} repetitions in {t:.1f} s "
+                     "(numpy float64, one row at a time)"}
+    return parity, cpu
+
+
 def rows_main(args) -> int:
     """Time one row reduction on its workload: algorithmic bytes (each input
     read once, the output written once) over the mean launch time, against
@@ -205,16 +288,19 @@ def rows_main(args) -> int:
     sys.path.insert(0, ROOT)
     import gemm_inputs as gi
     import dense_fp32_matrix_gemm_amd as g
-    from oracle import rows as R
 
     spec = ROW_OPS[args.rows]
     rows, width = spec["rows"], spec["width"]
     g.load()
-    x = gi.stored_matrix(spec["seed"], rows, width, dist="n01")
-    dy = gi.stored_matrix(spec["seed"] + 2, rows, width, dist="n01")
     scale, eps = 0.125, 1e-5
     if args.rows == "softmax-bwd":
-        x = R.softmax(x, width, width, scale).astype(np.float32)  # the forward output y
+        # the forward output y: seeded values in [0, 2/width), the range of a
+        # row of probabilities (the gradient is defined for any y)
+        x = (gi.stored_matrix(spec["seed"] + 1, rows, width, dist="u11") + np.float32(1.0)) \
+            * np.float32(1.0 / width)
+    else:
+        x = gi.stored_matrix(spec["seed"], rows, width, dist="n01")
+    dy = gi.stored_matrix(spec["seed"] + 2, rows, width, dist="n01")
     dx, ddy = torch.from_numpy(x).cuda(), torch.from_numpy(dy).cuda()
     out = torch.empty_like(dx)
     stream = torch.cuda.current_stream()
@@ -240,55 +326,14 @@ def rows_main(args) -> int:
 
     op = {"softmax": "softmax", "softmax-bwd": "softmax_backward", "normalize": "normalize",
           "normalize-bwd": "normalize_backward"}[args.rows]
-    nbytes = R.algorithmic_bytes(op, rows, width)
+    nbytes = row_bytes(op, rows, width)
     torch.cuda.synchronize()
     ms = _timed(step, args.steps, args.warmup)
     value = nbytes / (ms * 1e-3) / 1e9
 
-    # sampled parity: whole rows against the oracle (a row's causal mask
-    # follows its index r: alone, it is a group of width - r % width queries)
-    got = out.cpu().numpy()
-    pick = np.sort(np.random.default_rng(5).choice(rows, 64, replace=False))
-    if op == "softmax":
-        ref = np.stack([R.softmax(x[r:r + 1], width, width - r % width, scale)[0] for r in pick])
-        bound = 1e-5 * ref + 1e-8
-    elif op == "softmax_backward":
-        ref = R.softmax_backward(x[pick], dy[pick], width, scale)
-        S = np.sum(np.abs(dy[pick].astype(np.float64) * x[pick]), axis=1, keepdims=True)
-        bound = 1e-5 * scale * np.abs(x[pick]) * (np.abs(dy[pick]) + S) + 1e-9
-    elif op == "normalize":
-        ref = R.normalize(x[pick], width, eps)
-        bound = 1e-5 * (np.abs(ref) + 1.0)
-    else:
-        ref = R.normalize_backward(x[pick], dy[pick], width, eps)
-        a64, g64 = x[pick].astype(np.float64), dy[pick].astype(np.float64)
-        sigma = np.sqrt(a64.var(axis=1, keepdims=True) + eps)
-        xhat = (a64 - a64.mean(axis=1, keepdims=True)) / sigma
-        bound = 2e-5 * (np.abs(ref) + (np.abs(g64) + np.abs(g64).mean(axis=1, keepdims=True)
-                                       + np.abs(xhat) * np.abs(g64 * xhat).mean(axis=1, keepdims=True))
-                        / sigma) + 1e-9
-    ratio = np.abs(got[pick] - ref) / bound
-    parity = {"rows": int(len(pick)), "max_err_over_bound": float(np.max(ratio)),
-              "ok": bool(np.all(ratio <= 1.0))}
-
-    cpu = None
+    parity = cpu = None
     if not args.no_cpu_baseline:
-        sample = 1024
-        fn = {"softmax": lambda: R.softmax(x[:sample], width, width, scale),
-              "softmax_backward": lambda: R.softmax_backward(x[:sample], dy[:sample], width, scale),
-              "normalize": lambda: R.normalize(x[:sample], width, eps),
-              "normalize_backward": lambda: R.normalize_backward(x[:sample], dy[:sample], width,
-                                                                 eps)}[op]
-        reps, t = 0, 0.0
-        t0 = time.perf_counter()
-        while t < 10.0:
-            fn()
-            reps += 1
-            t = time.perf_counter() - t0
-        cpu = {"value": R.algorithmic_bytes(op, sample, width) * reps / t / 1e9, "unit": "GB/s",
-               "cores": 1, "kind": "oracle",
-               "sample": f"first {sample} of {rows} rows, {reps} repetitions in {t:.1f} s "
-                         "(numpy float64, one row at a time)"}
+        parity, cpu = rows_oracle_leg(op, x, dy, out.cpu().numpy(), rows, width, scale, eps)
 
     line = {
         "metric": f"row reduction HBM throughput ({op}, algorithmic bytes / s)",
@@ -414,26 +459,7 @@ def main(argv=None) -> int:
     ms = _timed(step, args.steps, args.warmup)
     value = flops / (ms * 1e-3) / 1e12
 
-    # sampled parity of the timed result (expected values from the oracle only)
-    parity = None
-    if not args.no_cpu_baseline:
-        import oracle
-        rows, cols = gi.sample_entries(w.M, w.N, 256, seed=23)
-        a0, b0, c0 = A, B, dC.cpu().numpy()
-        if batched:  # the last product of the batch
-            last = w.batch - 1
-            a0 = A[last, :w.a_dims[0] * w.lda_].reshape(w.a_dims[0], w.lda_)
-            b0 = B if w.shared_b else B[last, :w.b_dims[0] * w.ldb_].reshape(w.b_dims[0], w.ldb_)
-            c0 = c0[last, :w.M * w.ldc_].reshape(w.M, w.ldc_)
-        entries = oracle.load().entries_bf16 if mixed else oracle.load().entries
-        ref = entries(a0, b0, w.M, w.N, w.K, w.transA, w.transB, rows, cols)
-        if fused:
-            ref = oracle.load().epilogue((ref + bias[cols].astype(np.float64))[None, :], None,
-                                         act)[0]
-        got = c0[rows, cols].astype(np.float64)
-        ratio = np.abs(got - ref) / (1e-6 * w.K + 1e-5 * np.abs(ref))
-        parity = {"entries": int(rows.size), "max_err_over_bound": float(np.max(ratio)),
-                  "ok": bool(np.all(ratio <= 1.0))}
+    c_host = dC.cpu().numpy()
 
     kernel = "gemm_f32_" + ("mfma" if args.algo in ("auto", "mfma256", "mfma128", "mfma64") else args.algo)
     peak = MI355X_BF16_PEAK_TFLOPS if mixed else MI355X_FP32_PEAK_TFLOPS
@@ -529,9 +555,14 @@ def main(argv=None) -> int:
         tms = _timed(lambda: torch.mm(ta, tb, out=out), 10, 2)
         context["torch.mm"] = {"tflops": flops / (tms * 1e-3) / 1e12, "ms": tms}
 
-    cpu = None
-    if not args.no_cpu_baseline and not batched:
-        cpu = cpu_baseline(w, mixed=mixed)
+    # The CPU-baseline leg, the only place this script runs the oracle: the
+    # oracle timed on a sample of the workload, and a sampled check of the
+    # timed result against it.
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        parity = sampled_parity(w, A, B, c_host, mixed, bias if fused else None, act)
+        if not batched:
+            cpu = cpu_baseline(w, mixed=mixed)
 
     line = {
         "metric": ("mixed-precision GEMM TFLOPS (2MNK/s; bf16 operands, FP32 sums)" if mixed else
