@@ -23,7 +23,11 @@ cpu_baseline and parity form the CPU-baseline leg, the only part of this
 script that runs the oracle (skipped with --no-cpu-baseline).
 
 ``--algo bf16`` times the mixed-precision entry point instead (operands
-rounded to bf16, FP32 sums) against the dense bf16 matrix peak (2.5 PFLOP/s).
+rounded to bf16, FP32 sums) against the dense bf16 matrix peak (2.5 PFLOP/s);
+``--algo bf16packed`` times the product of operands packed beforehand
+(gemm_f32_pack_bf16, outside the timed region, like a framework's bf16
+copies of its weights), and reports the packing kernels' time and the
+end-to-end rate beside it.
 
 ``--copy-probe`` instead runs a plain device copy of known size, the
 scale reference for the HBM byte counters.  ``--gpus`` above 1 exits:
@@ -80,6 +84,7 @@ KERNEL_SOURCES = {
     "gemm_f32_tiled": ["gemm_simple.hip", "gemm_internal.hpp"],
     "gemm_f32_naive": ["gemm_simple.hip", "gemm_internal.hpp"],
     "gemm_f32_bf16": ["gemm_bf16.hip", "tile_common.hpp", "gemm_internal.hpp"],
+    "gemm_f32_bf16packed": ["gemm_bf16_packed.hip", "tile_common.hpp", "gemm_internal.hpp"],
     "rows_softmax_f32": ["rows.hip", "gemm_internal.hpp", "../../include/rows_f32.h"],
 }
 
@@ -363,9 +368,11 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--algo", default="auto",
-                    choices=["auto", "mfma", "mfma256", "mfma128", "mfma64", "fma", "tiled", "naive", "bf16"],
+                    choices=["auto", "mfma", "mfma256", "mfma128", "mfma64", "fma", "tiled", "naive", "bf16",
+                             "bf16packed"],
                     help="kernel family; bf16 times the mixed-precision entry point "
-                         "(operands rounded to bf16, FP32 sums)")
+                         "(operands rounded to bf16, FP32 sums), bf16packed its two-step form "
+                         "on operands packed beforehand")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -406,7 +413,8 @@ def main(argv=None) -> int:
     dB = torch.from_numpy(B).cuda()
     dC = torch.from_numpy(C).cuda()
     stream = torch.cuda.current_stream()
-    mixed = args.algo == "bf16"
+    mixed = args.algo in ("bf16", "bf16packed")
+    packed = args.algo == "bf16packed"
     algo_id = g.ALGOS["auto" if mixed else args.algo]
 
     batched = w.batch > 1
@@ -429,6 +437,16 @@ def main(argv=None) -> int:
     bias = gi.stored_matrix(2003, 1, w.N, dist="n002")[0] if fused else None
     dbias = torch.from_numpy(bias).cuda() if fused else None
     act = g.ACT_GELU if args.epilogue == "gelu" else g.ACT_NONE
+    # op(A) (M x K) and op(B) (K x N) as views of the stored operands
+    op_a = dA.reshape(-1, A.shape[-1])[:, :w.a_dims[1]] if not batched else None
+    op_b = dB.reshape(-1, B.shape[-1])[:, :w.b_dims[1]] if not batched else None
+    if not batched:
+        op_a = op_a.t() if w.transA else op_a
+        op_b = op_b.t() if w.transB else op_b
+    if packed:
+        pa = g.pack_bf16(op_a)       # M x K, k along the rows
+        pb = g.pack_bf16(op_b.t())   # N x K
+        torch.cuda.synchronize()
 
     def step(algo=algo_id, plain=False):
         if splitk and not plain:
@@ -439,6 +457,9 @@ def main(argv=None) -> int:
             st = g.gemm_f32_bias_act(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
                                      dC.data_ptr(), w.ldc_, w.transA, w.transB, dbias.data_ptr(),
                                      act, stream.cuda_stream)
+        elif packed and algo == algo_id and not plain:
+            st = g.gemm_f32_bf16_packed(w.M, w.N, w.K, pa.data_ptr(), pa.stride(0), pb.data_ptr(),
+                                        pb.stride(0), dC.data_ptr(), w.ldc_, stream.cuda_stream)
         elif mixed and algo == algo_id:
             st = g.gemm_f32_bf16(w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_,
                                  dC.data_ptr(), w.ldc_, w.transA, w.transB, stream.cuda_stream)
@@ -518,10 +539,7 @@ def main(argv=None) -> int:
                    "torch.mm": {"tflops": flops / (tms * 1e-3) / 1e12, "ms": tms},
                    "workspace_bytes": ws_bytes}
     elif not args.no_context and mixed:
-        ta = dA[:, :w.a_dims[1]]
-        tb = dB[:, :w.b_dims[1]]
-        ta = ta.t() if w.transA else ta
-        tb = tb.t() if w.transB else tb
+        ta, tb = op_a, op_b
         ha, hb = ta.to(torch.bfloat16), tb.to(torch.bfloat16)
         out16 = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
         out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
@@ -532,6 +550,19 @@ def main(argv=None) -> int:
                    {"tflops": flops / (t16 * 1e-3) / 1e12, "ms": t16},
                    "torch.mm f32": {"tflops": flops / (t32 * 1e-3) / 1e12, "ms": t32},
                    "gemm_f32 (FP32 MFMA)": {"tflops": flops / (mine * 1e-3) / 1e12, "ms": mine}}
+        if packed:
+            # the packing kernels (HBM-bound: 4 bytes read, 2 written per
+            # element) and the fused one-step entry point on the same inputs
+            tpa = _timed(lambda: g.pack_bf16(op_a, out=pa), 20, 5)
+            tpb = _timed(lambda: g.pack_bf16(op_b.t(), out=pb), 20, 5)
+            fused1 = _timed(lambda: step(algo_id, plain=True), 20, 5)
+            pbytes = 6 * (w.M * w.K + w.N * w.K)
+            context.update({
+                "pack A and B (gemm_f32_pack_bf16)": {"ms": tpa + tpb, "gbps": pbytes / ((tpa + tpb) * 1e-3) / 1e9},
+                "pack + product (end to end)": {"tflops": flops / ((ms + tpa + tpb) * 1e-3) / 1e12,
+                                                "ms": ms + tpa + tpb},
+                "gemm_f32_bf16 (one step, converts on every read)": {"tflops": flops / (fused1 * 1e-3) / 1e12,
+                                                                     "ms": fused1}})
     elif not args.no_context:
         context = {}
         for other in ("mfma", "fma", "tiled", "naive"):
@@ -565,7 +596,9 @@ def main(argv=None) -> int:
             cpu = cpu_baseline(w, mixed=mixed)
 
     line = {
-        "metric": ("mixed-precision GEMM TFLOPS (2MNK/s; bf16 operands, FP32 sums)" if mixed else
+        "metric": ("mixed-precision GEMM TFLOPS (2MNK/s; bf16 operands packed beforehand, FP32 sums)"
+                   if packed else
+                   "mixed-precision GEMM TFLOPS (2MNK/s; bf16 operands, FP32 sums)" if mixed else
                    "FP32 GEMM TFLOPS (2MNK/s) and % of MI355X FP32 peak at N=4096"),
         "value": value,
         "unit": "TFLOPS",

@@ -4,8 +4,9 @@ The product runs in hand-written HIP kernels behind a C ABI
 (``include/gemm_f32.h`` and ``include/rows_f32.h``, library
 ``libgemm_f32.so``).  This package is the thin Python side: the raw ABI
 calls under their C names, and tensor-level helpers (``matmul``, ``bmm``,
-``linear``, ``matmul_splitk``, ``softmax``, ``softmax_backward``,
-``normalize``, ``normalize_backward``) that take PyTorch device tensors,
+``linear``, ``matmul_splitk``, ``matmul_bf16``, ``pack_bf16``,
+``matmul_bf16_packed``, ``softmax``, ``softmax_backward``, ``normalize``,
+``normalize_backward``) that take PyTorch device tensors,
 read their pointers, strides and the current stream, and call the library.
 PyTorch owns memory and streams; every step of the computation runs in the
 library's kernels.
@@ -14,14 +15,15 @@ library's kernels.
 from __future__ import annotations
 
 from ._lib import (ACT_GELU, ACT_NONE, ALGOS, LibraryNotBuilt, gemm_f32, gemm_f32_bf16,
-                   gemm_f32_bias_act,
+                   gemm_f32_bf16_packed, gemm_f32_bias_act, gemm_f32_pack_bf16,
                    gemm_f32_ex, gemm_f32_naive, gemm_f32_splitk, gemm_f32_splitk_workspace_size,
                    gemm_f32_strerror, gemm_f32_strided_batched, gemm_f32_version, library_path,
                    load, rows_normalize_backward_f32, rows_normalize_f32,
                    rows_softmax_backward_f32, rows_softmax_f32)
 
 __all__ = ["ACT_GELU", "ACT_NONE", "ALGOS", "GemmError", "LibraryNotBuilt", "bmm", "gemm_f32",
-           "gemm_f32_bf16", "gemm_f32_bias_act", "gemm_f32_ex", "linear",
+           "gemm_f32_bf16", "gemm_f32_bf16_packed", "gemm_f32_bias_act", "gemm_f32_ex",
+           "gemm_f32_pack_bf16", "linear", "matmul_bf16", "matmul_bf16_packed", "pack_bf16",
            "gemm_f32_naive", "gemm_f32_splitk", "gemm_f32_splitk_workspace_size",
            "gemm_f32_strerror", "gemm_f32_strided_batched",
            "gemm_f32_version", "library_path", "load", "matmul", "matmul_splitk",
@@ -36,12 +38,14 @@ class GemmError(RuntimeError):
         super().__init__(f"gemm_f32 status {status}: {gemm_f32_strerror(status)}")
 
 
-def _check_tensor(t, name, device=None, dims=2):
-    """A float32 tensor on the GPU (and on ``device`` if given): the library
-    dereferences its pointer on the device, so anything else is refused here."""
+def _check_tensor(t, name, device=None, dims=2, dtype=None):
+    """A float32 (or ``dtype``) tensor on the GPU (and on ``device`` if
+    given): the library dereferences its pointer on the device, so anything
+    else is refused here."""
     import torch
-    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
-        raise TypeError(f"{name} must be a float32 tensor")
+    dtype = torch.float32 if dtype is None else dtype
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise TypeError(f"{name} must be a {str(dtype).replace('torch.', '')} tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if device is not None and t.device != device:
@@ -203,6 +207,93 @@ def matmul_splitk(a, b, splits: int, out=None, workspace=None, stream=None):
         stream = torch.cuda.current_stream(a.device).cuda_stream
     st = gemm_f32_splitk(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
                          ta, tb, splits, ws_ptr, ws_bytes, stream)
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+# ------------------------------------------------------------ mixed precision ---
+
+def _gemm_out(out, M, N, device):
+    import torch
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=device)
+    _check_tensor(out, "out", device)
+    if out.shape != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be an M x N float32 tensor with unit column stride")
+    return out, (max(out.stride(0), N, 1) if M > 1 else max(N, 1))
+
+
+def matmul_bf16(a, b, out=None, stream=None):
+    """out = a @ b with each operand element rounded to bf16 on the way in
+    and FP32 sums (gemm_f32_bf16); a, b and out are float32 tensors as for
+    ``matmul``."""
+    _check_tensor(a, "a")
+    _check_tensor(b, "b", a.device)
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
+    out, ldc = _gemm_out(out, M, N, a.device)
+    ta, lda = operand_layout(a)
+    tb, ldb = operand_layout(b)
+    st = gemm_f32_bf16(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
+                       ta, tb, _stream(a, stream))
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def pack_bf16(x, out=None, stream=None):
+    """A bf16 copy of the float32 matrix ``x`` (row-major or a transposed
+    view), rounded to nearest with ties to even (gemm_f32_pack_bf16).
+
+    The result is a row-major bf16 view whose rows are padded to a multiple
+    of 8 elements, the layout ``matmul_bf16_packed`` copies fastest.  To use
+    a @ b on packed operands: ``matmul_bf16_packed(pack_bf16(a),
+    pack_bf16(b.t()))``.  ``out`` (optional) is a bf16 tensor of x's shape
+    with unit column stride.
+    """
+    import torch
+
+    _check_tensor(x, "x")
+    rows, cols = x.shape
+    trans, lds = operand_layout(x)
+    if out is None:
+        ld = max(8, (cols + 7) // 8 * 8)
+        out = torch.empty((rows, ld), dtype=torch.bfloat16, device=x.device)[:, :cols]
+    _check_tensor(out, "out", x.device, dtype=torch.bfloat16)
+    if out.shape != x.shape or (cols > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a bf16 tensor of x's shape with unit column stride")
+    ldd = max(out.stride(0), cols, 1) if rows > 1 else max(cols, 1)
+    st = gemm_f32_pack_bf16(rows, cols, x.data_ptr(), lds, trans, out.data_ptr(), ldd,
+                            _stream(x, stream))
+    if st != 0:
+        raise GemmError(st)
+    return out
+
+
+def matmul_bf16_packed(a, b, out=None, stream=None):
+    """out = a @ b.T for packed bf16 operands (gemm_f32_bf16_packed): ``a`` is
+    M x K and ``b`` N x K, both bf16 with unit column stride (as
+    ``pack_bf16`` makes them); the products are summed in FP32 into the
+    float32 M x N ``out``."""
+    import torch
+
+    _check_tensor(a, "a", dtype=torch.bfloat16)
+    _check_tensor(b, "b", a.device, dtype=torch.bfloat16)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K2 != K:
+        raise ValueError(f"a and b must have the same number of columns: {tuple(a.shape)}, {tuple(b.shape)}")
+    for t, name in ((a, "a"), (b, "b")):
+        if t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit column stride")
+    lda = max(a.stride(0), K, 1) if M > 1 else max(K, 1)
+    ldb = max(b.stride(0), K, 1) if N > 1 else max(K, 1)
+    out, ldc = _gemm_out(out, M, N, a.device)
+    st = gemm_f32_bf16_packed(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc,
+                              _stream(a, stream))
     if st != 0:
         raise GemmError(st)
     return out

@@ -32,6 +32,8 @@ SIGNATURES = {
     "gemm_f32_bias_act": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                  _ptr, _int, _ptr]),
     "gemm_f32_bf16": (_int, _GEMM_ARGS),
+    "gemm_f32_pack_bf16": (_int, [_i64, _i64, _ptr, _i64, _int, _ptr, _i64, _ptr]),
+    "gemm_f32_bf16_packed": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr]),
     "gemm_f32_splitk": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                _i64, _ptr, _i64, _ptr]),
     "gemm_f32_splitk_workspace_size": (_i64, [_i64, _i64, _i64, _i64]),
@@ -109,6 +111,16 @@ def gemm_f32_bias_act(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, bias, act
 def gemm_f32_bf16(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream) -> int:
     """C = op(A) . op(B) with operands rounded to bf16, FP32 sums and output."""
     return _call("gemm_f32_bf16", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, stream)
+
+
+def gemm_f32_pack_bf16(rows, cols, src, lds, trans, dst, ldd, stream) -> int:
+    """dst = bf16 bit patterns of op(src) (rows x cols, leading dimension ldd)."""
+    return _call("gemm_f32_pack_bf16", rows, cols, src, lds, trans, dst, ldd, stream)
+
+
+def gemm_f32_bf16_packed(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    """C = A . B^T on packed bf16 operands (A M x K, B N x K), FP32 sums and C."""
+    return _call("gemm_f32_bf16_packed", M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, splits, workspace,

@@ -204,6 +204,48 @@ int gemm_f32_bf16(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     return err == hipSuccess ? 0 : int(err);
 }
 
+int gemm_f32_pack_bf16(int64_t rows, int64_t cols, const float *src, int64_t lds, int trans,
+                       uint16_t *dst, int64_t ldd, void *stream)
+{
+    if (rows < 0 || rows > kDimLimit) return -1;
+    if (cols < 0 || cols > kDimLimit) return -2;
+    if (src == nullptr && rows * cols > 0) return -3;
+    if (trans != 0 && trans != 1) return -5;
+    const int64_t src_row = trans ? rows : cols;  // length of a stored row of src
+    if (lds < (src_row > 1 ? src_row : 1) || lds > kDimLimit) return -4;
+    if (dst == nullptr && rows * cols > 0) return -6;
+    if (ldd < (cols > 1 ? cols : 1) || ldd > kDimLimit) return -7;
+    if (rows == 0 || cols == 0) return 0;
+    const hipError_t err = gemmf32::launch_pack_bf16(int(rows), int(cols), src, lds, trans, dst, ldd,
+                                                     static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? 0 : int(err);
+}
+
+int gemm_f32_bf16_packed(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                         const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    if (M < 0 || M > kDimLimit) return -kArgM;
+    if (N < 0 || N > kDimLimit) return -kArgN;
+    if (K < 0 || K > kDimLimit) return -kArgK;
+    if (A == nullptr && M * K > 0) return -kArgA;
+    if (lda < (K > 1 ? K : 1) || lda > kDimLimit) return -kArgLda;
+    if (B == nullptr && N * K > 0) return -kArgB;
+    if (ldb < (K > 1 ? K : 1) || ldb > kDimLimit) return -kArgLdb;
+    if (C == nullptr && M * N > 0) return -kArgC;
+    if (ldc < (N > 1 ? N : 1) || ldc > kDimLimit) return -kArgLdc;
+    if (M == 0 || N == 0) return 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (K == 0) {
+        const Problem z{int(M), int(N), 0, nullptr, 1, nullptr, 1, C, ldc, 0, 0};
+        err = gemmf32::launch_zero_fill(z, s);
+    } else {
+        const gemmf32::PackedProblem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc};
+        err = gemmf32::launch_bf16_packed(p, s);
+    }
+    return err == hipSuccess ? 0 : int(err);
+}
+
 int64_t gemm_f32_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int64_t splits)
 {
     if (M < 0 || M > kDimLimit) return -1;
@@ -258,6 +300,6 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda
     return err == hipSuccess ? 0 : int(err);
 }
 
-int gemm_f32_version(void) { return 10400; }
+int gemm_f32_version(void) { return 10500; }
 
 }  // extern "C"

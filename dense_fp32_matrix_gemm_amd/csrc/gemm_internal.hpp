@@ -44,6 +44,25 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
 // Operands rounded to bf16 (nearest, ties to even), bf16 matrix-core
 // products, FP32 sums and output.  Ignores batch, bias and act.
 hipError_t launch_bf16(const Problem &p, hipStream_t stream, int tile = 0);
+// A product of two packed bf16 operands (bit patterns): A is M x K and B is
+// N x K, both with k along their rows; C = A . B^T in FP32.
+struct PackedProblem {
+    int M, N, K;
+    const uint16_t *A;
+    int64_t lda;
+    const uint16_t *B;
+    int64_t ldb;
+    float *C;
+    int64_t ldc;
+};
+// tile: 0 chooses by problem size; 256 (256 x 256) or 128 forces that tile
+// (256 falls back to 128 beyond K = 16384).  Assumes M, N, K >= 1.
+hipError_t launch_bf16_packed(const PackedProblem &p, hipStream_t stream, int tile = 0);
+// dst[r * ldd + c] = bf16 bits of op(src)[r][c] (nearest, ties to even) for
+// r < rows, c < cols; op(src) = src (stored rows x cols) or, with trans,
+// src^T (stored cols x rows).  Assumes rows, cols >= 1.
+hipError_t launch_pack_bf16(int rows, int cols, const float *src, int64_t lds, int trans, uint16_t *dst,
+                            int64_t ldd, hipStream_t stream);
 // C[i][j] = sum over s < splits, in increasing s, of ws[s*M*N + i*N + j]:
 // the fixed-order sum of split-k partial products (packed M x N each).
 hipError_t launch_splitk_reduce(const float *ws, int splits, int M, int N, float *C, int64_t ldc,

@@ -156,6 +156,50 @@ int gemm_f32_bf16(int64_t M, int64_t N, int64_t K,
                   float *C, int64_t ldc,
                   int transA, int transB, void *stream);
 
+/* Mixed precision in two steps, rounding each operand once: pack it with
+ * gemm_f32_pack_bf16, then multiply packed operands with
+ * gemm_f32_bf16_packed.  Same arithmetic as gemm_f32_bf16 (the Smallem
+ * page, "Rendre le GPU rapide", section "Les Tensor Cores": operands rounded
+ * to bf16, sums and C in FP32); the same page's comparison with PyTorch
+ * notes that keeping the 16-bit copies, as PyTorch does, saves converting on
+ * every read.  A packed operand is a row-major array of bf16 bit patterns
+ * (uint16_t: the upper half of the FP32 encoding) with k along its rows. */
+
+/* dst[r*ldd + c] = bf16(op(src)[r][c]) for r < rows, c < cols, rounded to
+ * nearest with ties to even; columns c >= cols of dst are not written.
+ * op(src) = src, stored rows x cols (lds >= max(1, cols)), when trans == 0;
+ * src^T, with src stored cols x rows (lds >= max(1, rows)), when trans == 1.
+ * To pack A of gemm_f32 for gemm_f32_bf16_packed: rows = M, cols = K,
+ * trans = transA.  To pack B (K x N): rows = N, cols = K, trans = !transB.
+ * src (FP32) and dst are device arrays the caller owns; they must not
+ * overlap.  ldd >= max(1, cols); an ldd that is a multiple of 8 with a
+ * 16-byte aligned dst lets the product copy whole 16-byte vectors.
+ * Returns 0, or -1 rows / -2 cols negative or >= 2^31, -3 src NULL with
+ * rows*cols > 0, -4 lds too small or >= 2^31, -5 trans not 0 or 1, -6 dst
+ * NULL with rows*cols > 0, -7 ldd < max(1, cols) or >= 2^31 (checked on the
+ * host before any HIP call), or a positive hipError_t from the launch.
+ * rows == 0 or cols == 0 writes nothing.  Asynchronous on `stream`. */
+int gemm_f32_pack_bf16(int64_t rows, int64_t cols, const float *src, int64_t lds, int trans,
+                       uint16_t *dst, int64_t ldd, void *stream);
+
+/* C = A . B^T with A (M x K, lda >= max(1, K)) and B (N x K, ldb >= max(1,
+ * K)) packed bf16 operands, the products summed in FP32 and C (M x N, ldc >=
+ * max(1, N)) written in FP32, overwritten.  C[i][j] = sum over k of
+ * A[i][k] * B[j][k].  Results agree with the exact sum of the products to
+ * within 1e-6*K + 1e-5*|C| elementwise for operands of magnitude <= 1, and
+ * equal it exactly under the conditions given for gemm_f32_bf16.  Device
+ * arrays the caller owns; C must not overlap A or B.  Codes -1 .. -9 as for
+ * gemm_f32's first nine arguments (the stored rows of A and B hold K
+ * elements); M == 0 or N == 0 writes nothing; K == 0 writes zeros.  Interior
+ * tiles copy whole 16-byte vectors straight into LDS when A and B are
+ * 16-byte aligned and lda, ldb are multiples of 8; otherwise every tile is
+ * staged through registers (same results, slower).  Runs on the bf16 matrix
+ * cores (v_mfma_f32_32x32x16_bf16). */
+int gemm_f32_bf16_packed(int64_t M, int64_t N, int64_t K,
+                         const uint16_t *A, int64_t lda,
+                         const uint16_t *B, int64_t ldb,
+                         float *C, int64_t ldc, void *stream);
+
 /* Split-k product: C = op(A) . op(B) as in gemm_f32, computed as `splits`
  * partial products over consecutive runs of k followed by their sum.  The
  * Smallem page ("Rendre le GPU rapide", section "Ce qui n'a pas marche")

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert g.gemm_f32_version() == 10400
+    assert g.gemm_f32_version() == 10500
 
 
 def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
@@ -134,7 +134,7 @@ def test_operand_layout_from_strides():
 def test_header_is_plain_c():
     """The public header compiles as C with no HIP headers on the include path."""
     import subprocess
-    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10400 ? 0 : 1;}\n"
+    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10500 ? 0 : 1;}\n"
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
                        input=src, capture_output=True, text=True)
@@ -268,8 +268,63 @@ def test_tensor_helpers_refuse_host_tensors():
     x = torch.ones(4, 4)
     for call in (lambda: g.matmul(x, x), lambda: g.linear(x, x), lambda: g.matmul_splitk(x, x, 2),
                  lambda: g.bmm(x[None], x[None]), lambda: g.softmax(x), lambda: g.normalize(x),
-                 lambda: g.softmax_backward(x, x), lambda: g.normalize_backward(x, x)):
+                 lambda: g.softmax_backward(x, x), lambda: g.normalize_backward(x, x),
+                 lambda: g.matmul_bf16(x, x), lambda: g.pack_bf16(x)):
         with pytest.raises(ValueError, match="device tensor"):
             call()
+    xb = x.to(torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        g.matmul_bf16_packed(xb, xb)
+    with pytest.raises(TypeError, match="bfloat16"):
+        g.matmul_bf16_packed(x, x)
     with pytest.raises(TypeError, match="float32"):
         g.matmul(x.double(), x.double())
+
+
+# ------------------------------------------------------------- packed bf16 ---
+
+def pack(rows=4, cols=6, src=FAKE, lds=None, trans=0, dst=FAKE, ldd=None):
+    lds = max(1, rows if trans else cols) if lds is None else lds
+    ldd = max(1, cols) if ldd is None else ldd
+    return g.gemm_f32_pack_bf16(rows, cols, src, lds, trans, dst, ldd, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(rows=-1), -1), (dict(rows=BIG), -1), (dict(cols=-1), -2), (dict(cols=BIG), -2),
+    (dict(src=None), -3), (dict(lds=5), -4), (dict(lds=BIG), -4),
+    (dict(trans=1, lds=3), -4),            # transposed: src stored cols x rows, lds >= rows
+    (dict(trans=2), -5), (dict(trans=-1), -5),
+    (dict(dst=None), -6), (dict(ldd=5), -7), (dict(ldd=BIG), -7),
+    (dict(rows=0, ldd=0), -7),             # ldd >= 1 even when nothing is written
+])
+def test_pack_bf16_invalid_arguments(kwargs, code):
+    assert pack(**kwargs) == code
+
+
+def test_pack_bf16_quick_return_without_launch():
+    assert pack(rows=0, src=None, dst=None) == 0
+    assert pack(cols=0, src=None, dst=None, lds=1, ldd=1) == 0
+
+
+def packed(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None):
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, K) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    return g.gemm_f32_bf16_packed(M, N, K, A, lda, B, ldb, C, ldc, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(M=-1), -1), (dict(N=BIG), -2), (dict(K=-1), -3), (dict(K=BIG), -3),
+    (dict(A=None), -4), (dict(lda=3), -5), (dict(lda=BIG), -5),
+    (dict(B=None), -6), (dict(ldb=3), -7),  # B is N x K: ldb >= K
+    (dict(N=9, ldb=3), -7),
+    (dict(C=None), -8), (dict(ldc=3), -9), (dict(ldc=BIG), -9),
+])
+def test_bf16_packed_invalid_arguments(kwargs, code):
+    assert packed(**kwargs) == code
+    assert g.gemm_f32_strerror(code).startswith(f"invalid argument {-code} ")
+
+
+def test_bf16_packed_quick_return_without_launch():
+    assert packed(M=0, A=None, C=None) == 0
+    assert packed(N=0, B=None, C=None) == 0
