@@ -10,8 +10,8 @@
 // choice.  Rounding once pays off on gfx950 because a bf16 stage is short:
 // a 256 x 256 x 32 stage is about a thousand matrix-core cycles, too short
 // for register-staged FP32 loads to hide their latency, while bf16 tiles
-// copied straight into LDS (global_load_lds_dwordx4) can be kept three
-// stages ahead in a four-buffer ring at half the bytes.
+// copied straight into LDS (global_load_lds_dwordx4) move half the bytes
+// with no register or LDS-write instructions.
 //
 // Product kernel layout:
 //  * A BM x BN tile of C per workgroup of WAVES_M x WAVES_N waves; each wave
@@ -368,12 +368,14 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
         }
 }
 
-// Large: 256 x 256, 8 waves of 64 x 128, one accumulator.  Small: 128 x
-// 128, 8 waves of 32 x 64, runs of 128 k summed into a fresh partial first
-// (about 100 registers, so two workgroups share a CU).  Both: 32-k stages in
-// a four-buffer ring.
+// Large: 256 x 256, 8 waves of 64 x 128, one accumulator, 64-k stages in two
+// buffers (128 KB of LDS; measured against 32-k stages in a four-buffer ring
+// at S4k: 1104 vs 1067 TFLOP/s, the barrier count halved mattering more
+// than the deeper ring).  Small: 128 x 128, 8 waves of 32 x 64, 32-k stages
+// in a four-buffer ring, runs of 128 k summed into a fresh partial first
+// (about 100 registers, so two workgroups share a CU).
 #ifndef GEMM_PACKED_LARGE_CONFIG
-#define GEMM_PACKED_LARGE_CONFIG 256, 256, 32, 4, 2, 4, 4, 0
+#define GEMM_PACKED_LARGE_CONFIG 256, 256, 64, 4, 2, 2, 4, 0
 #endif
 #ifndef GEMM_PACKED_SMALL_CONFIG
 #define GEMM_PACKED_SMALL_CONFIG 128, 128, 32, 4, 2, 4, 8, 4
@@ -381,8 +383,11 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
 using Large = Config<GEMM_PACKED_LARGE_CONFIG>;
 using Small = Config<GEMM_PACKED_SMALL_CONFIG>;
 
+// The large tile from one tile per CU: below that (e.g. 8192 x 1024, 128
+// large tiles) half the CUs would idle, and 128 x 128 tiles are faster
+// (749 vs 682 TFLOP/s).
 #ifndef GEMM_PACKED_LARGE_FROM
-#define GEMM_PACKED_LARGE_FROM 128
+#define GEMM_PACKED_LARGE_FROM 256
 #endif
 constexpr int kLargeMaxK = 16384;  // beyond this an unchunked sum drifts towards the 1e-6 bound
 
@@ -417,27 +422,43 @@ __device__ __forceinline__ u16 bf16_bits(float x)
     return __builtin_bit_cast(u16, __bf16(x));  // v_cvt_pk_bf16_f32: nearest, ties to even
 }
 
-// dst[r][c] = bf16(src[r][c]): each lane rounds four consecutive columns,
-// consecutive lanes take consecutive column groups.  VEC: 16-byte source
-// and 8-byte destination vectors are aligned.
+// dst[r][c] = bf16(src[r][c]).  Workgroup (x, y) rounds columns
+// [x * kRowChunk, +kRowChunk) of rows y, y + gridDim.y, ...: each lane takes
+// four groups of four consecutive columns kPackThreads groups apart, so a
+// wave reads 1 KB contiguous per load and each lane has four loads in
+// flight.  VEC: 16-byte source and 8-byte destination vectors are aligned.
+constexpr int kRowUnroll = 4;
+constexpr int kRowChunk = 4 * kPackThreads * kRowUnroll;  // columns per workgroup
+
 template <bool VEC>
 __global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(int rows, int cols, const float *__restrict__ src,
                                                                  int64_t lds, u16 *__restrict__ dst, int64_t ldd)
 {
-    const int groups = (cols + 3) / 4;
-    const int64_t total = int64_t(rows) * groups;
-    for (int64_t g = int64_t(blockIdx.x) * kPackThreads + threadIdx.x; g < total;
-         g += int64_t(gridDim.x) * kPackThreads) {
-        const int r = int(g / groups), c = 4 * int(g % groups);
-        const float *s = src + int64_t(r) * lds + c;
-        u16 *d = dst + int64_t(r) * ldd + c;
-        if (VEC && c + 3 < cols) {
-            const v4f x = *reinterpret_cast<const v4f *>(s);
-            const unsigned lo = unsigned(bf16_bits(x[0])) | (unsigned(bf16_bits(x[1])) << 16);
-            const unsigned hi = unsigned(bf16_bits(x[2])) | (unsigned(bf16_bits(x[3])) << 16);
-            *reinterpret_cast<v2u *>(d) = v2u{lo, hi};
-        } else {
-            for (int e = 0; e < 4 && c + e < cols; ++e) d[e] = bf16_bits(s[e]);
+    const int64_t c0 = int64_t(blockIdx.x) * kRowChunk + 4 * int(threadIdx.x);  // cols may approach 2^31
+    for (int r = blockIdx.y; r < rows; r += gridDim.y) {
+        const float *s = src + int64_t(r) * lds;
+        u16 *d = dst + int64_t(r) * ldd;
+        v4f x[kRowUnroll];
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const int64_t c = c0 + 4 * kPackThreads * u;
+            if (VEC && c + 3 < cols) {
+                x[u] = *reinterpret_cast<const v4f *>(s + c);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[u][e] = (c + e < cols) ? s[c + e] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const int64_t c = c0 + 4 * kPackThreads * u;
+            if (VEC && c + 3 < cols) {
+                const unsigned lo = unsigned(bf16_bits(x[u][0])) | (unsigned(bf16_bits(x[u][1])) << 16);
+                const unsigned hi = unsigned(bf16_bits(x[u][2])) | (unsigned(bf16_bits(x[u][3])) << 16);
+                *reinterpret_cast<v2u *>(d + c) = v2u{lo, hi};
+            } else {
+                for (int e = 0; e < 4 && c + e < cols; ++e) d[c + e] = bf16_bits(x[u][e]);
+            }
         }
     }
 }
@@ -521,13 +542,17 @@ hipError_t launch_pack_bf16(int rows, int cols, const float *src, int64_t lds, i
     // A grid of up to 64 workgroups per CU's worth; the kernels stride over the rest.
     constexpr int64_t kMaxBlocks = 256 * 64;
     if (!trans) {
-        const int64_t total = int64_t(rows) * ((cols + 3) / 4);
-        int64_t blocks = (total + kPackThreads - 1) / kPackThreads;
-        if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+        // x: column chunks (at most 2^31 / kRowChunk); y: rows, strided
+        // beyond the grid's y limit, and capped so that about kMaxBlocks
+        // workgroups are launched in all.
+        const int64_t gx = (int64_t(cols) + kRowChunk - 1) / kRowChunk;
+        int64_t gy = kMaxBlocks / gx;
+        gy = gy < 1 ? 1 : gy > rows ? rows : gy > kMaxGridY ? kMaxGridY : gy;
+        const dim3 grid{unsigned(gx), unsigned(gy), 1u};
         if (vec)
-            pack_rows_kernel<true><<<dim3(unsigned(blocks)), dim3(kPackThreads), 0, s>>>(rows, cols, src, lds, dst, ldd);
+            pack_rows_kernel<true><<<grid, dim3(kPackThreads), 0, s>>>(rows, cols, src, lds, dst, ldd);
         else
-            pack_rows_kernel<false><<<dim3(unsigned(blocks)), dim3(kPackThreads), 0, s>>>(rows, cols, src, lds, dst, ldd);
+            pack_rows_kernel<false><<<grid, dim3(kPackThreads), 0, s>>>(rows, cols, src, lds, dst, ldd);
     } else {
         const int64_t tiles = int64_t((rows + kPackTile - 1) / kPackTile) * ((cols + kPackTile - 1) / kPackTile);
         const int64_t blocks = tiles < kMaxBlocks ? tiles : kMaxBlocks;

@@ -89,7 +89,8 @@ def run_pack(x_stored, rows, cols, lds, trans, ldd, offs=(0, 0)):
     return dst_t.cpu().numpy().view(np.uint16)[offs[1]:].reshape(rows, ldd)
 
 
-PACK_SHAPES = [(1, 1), (3, 5), (64, 64), (65, 130), (200, 96), (257, 1000), (1000, 33)]
+PACK_SHAPES = [(1, 1), (3, 5), (64, 64), (65, 130), (200, 96), (257, 1000), (1000, 33), (3, 9000),
+               (20000, 5)]
 
 
 @pytest.mark.parametrize("shape", PACK_SHAPES, ids=lambda s: "x".join(map(str, s)))
