@@ -354,7 +354,11 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
     }
 
     // Lane l of a 32 x 32 block holds column l % 32 and, in accumulator slot
-    // v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.
+    // v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.  (Swapping the operands
+    // would give each lane four consecutive columns, one 16-byte store instead
+    // of four 4-byte ones, but each store instruction then covers 32 rows of
+    // 32 bytes instead of 2 rows of 128: measured slower, 1084 vs 1109
+    // TFLOP/s at S4k.)
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -371,16 +375,23 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
 // Large: 256 x 256, 8 waves of 64 x 128, one accumulator, 64-k stages in two
 // buffers (128 KB of LDS; measured against 32-k stages in a four-buffer ring
 // at S4k: 1104 vs 1067 TFLOP/s, the barrier count halved mattering more
-// than the deeper ring).  Small: 128 x 128, 8 waves of 32 x 64, 32-k stages
+// than the deeper ring).  Mid: 256 x 128, 8 waves of 64 x 64, otherwise the
+// same (96 KB), for grids with fewer large tiles than CUs (8192 x 1024 x
+// 4096: 900 vs 750 TFLOP/s on the small tile, whose 32-k stages it also
+// beats).  Small: 128 x 128, 8 waves of 32 x 64, 32-k stages
 // in a four-buffer ring, runs of 128 k summed into a fresh partial first
 // (about 100 registers, so two workgroups share a CU).
 #ifndef GEMM_PACKED_LARGE_CONFIG
 #define GEMM_PACKED_LARGE_CONFIG 256, 256, 64, 4, 2, 2, 4, 0
 #endif
+#ifndef GEMM_PACKED_MID_CONFIG
+#define GEMM_PACKED_MID_CONFIG 256, 128, 64, 4, 2, 2, 4, 0
+#endif
 #ifndef GEMM_PACKED_SMALL_CONFIG
 #define GEMM_PACKED_SMALL_CONFIG 128, 128, 32, 4, 2, 4, 8, 4
 #endif
 using Large = Config<GEMM_PACKED_LARGE_CONFIG>;
+using Mid = Config<GEMM_PACKED_MID_CONFIG>;
 using Small = Config<GEMM_PACKED_SMALL_CONFIG>;
 
 // The large tile from one tile per CU: below that (e.g. 8192 x 1024, 128
@@ -521,13 +532,24 @@ __global__ __launch_bounds__(kPackThreads) void pack_transposed_kernel(int rows,
 
 hipError_t launch_bf16_packed(const PackedProblem &p, hipStream_t s, int tile)
 {
+    // The largest tile that still gives every CU a tile of its own (and
+    // wastes at most a quarter of its area past the edges of C).
+    auto tiles = [&](int bm, int bn) { return int64_t(ceil_div(p.M, bm)) * ceil_div(p.N, bn); };
+    auto fits = [&](int bm, int bn) { return 4 * int64_t(p.M) * p.N >= 3 * tiles(bm, bn) * bm * bn; };
     if (tile == 0) {
-        const int64_t tiles = int64_t(ceil_div(p.M, Large::BM)) * ceil_div(p.N, Large::BN);
-        const bool fits = 4 * int64_t(p.M) * p.N >= 3 * tiles * Large::BM * Large::BN;
-        tile = (tiles >= GEMM_PACKED_LARGE_FROM && fits && p.K <= kLargeMaxK) ? Large::BM : Small::BM;
+        if (p.K > kLargeMaxK)
+            tile = Small::BM * Small::BN;
+        else if (tiles(Large::BM, Large::BN) >= GEMM_PACKED_LARGE_FROM && fits(Large::BM, Large::BN))
+            tile = Large::BM * Large::BN;
+        else if (tiles(Mid::BM, Mid::BN) >= GEMM_PACKED_LARGE_FROM && fits(Mid::BM, Mid::BN))
+            tile = Mid::BM * Mid::BN;
+        else
+            tile = Small::BM * Small::BN;
     }
-    if (tile == Large::BM && p.K <= kLargeMaxK)
+    if (tile == Large::BM * Large::BN && p.K <= kLargeMaxK)
         dispatch<Large>(p, s);
+    else if (tile == Mid::BM * Mid::BN && p.K <= kLargeMaxK)
+        dispatch<Mid>(p, s);
     else
         dispatch<Small>(p, s);
     return hipGetLastError();

@@ -55,8 +55,9 @@ struct PackedProblem {
     float *C;
     int64_t ldc;
 };
-// tile: 0 chooses by problem size; 256 (256 x 256) or 128 forces that tile
-// (256 falls back to 128 beyond K = 16384).  Assumes M, N, K >= 1.
+// tile: 0 chooses by problem size; a tile area (65536 for 256 x 256, 32768
+// for 256 x 128, 16384 for 128 x 128) forces that tile (the first two fall
+// back to 128 x 128 beyond K = 16384).  Assumes M, N, K >= 1.
 hipError_t launch_bf16_packed(const PackedProblem &p, hipStream_t stream, int tile = 0);
 // dst[r * ldd + c] = bf16 bits of op(src)[r][c] (nearest, ties to even) for
 // r < rows, c < cols; op(src) = src (stored rows x cols) or, with trans,

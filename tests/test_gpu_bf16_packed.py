@@ -160,10 +160,12 @@ def packed_case(oracle, M, N, K, dist, seed, pad=(0, 0)):
     return Ab, Bb, ref
 
 
-# The last shapes have enough 256 x 256 tiles to take the large tile, with
-# partial tiles in M and N, and a partial last stage (K % 32 != 0).
+# 4000 x 2000 and 3001 x 2817 take the 256 x 128 tile and 4097 x 4000 the
+# 256 x 256 tile, each with partial tiles in M and N and a partial last
+# stage; the others the 128 x 128 tile.
 SHAPES = [(1, 1, 1), (37, 45, 29), (128, 128, 32), (129, 257, 95), (300, 200, 512),
-          (1000, 1000, 1000), (2049, 700, 77), (3001, 2817, 100), (2816, 3072, 96)]
+          (1000, 1000, 1000), (2049, 700, 77), (4000, 2000, 100), (3001, 2817, 100),
+          (4097, 4000, 100)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
