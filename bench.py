@@ -4,7 +4,9 @@
 
 One step is one C = A.B of the workload (default: the 4096^3 square
 product the throughput metric is quoted on), with A, B and C resident in
-HBM before timing starts.  W untimed steps, then exactly K steps between
+HBM before timing starts.  W untimed steps (by default at least 300 and at
+least 0.3 s of them, so that short kernels are timed at a settled clock;
+the line reports the count), then exactly K steps between
 two device synchronisations, timed with HIP events recorded on the stream
 the library launches on (PyTorch's current stream).  Prints ONE JSON line.
 
@@ -138,6 +140,33 @@ def _timed(fn, steps: int, warmup: int):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def _warm_up(fn, warmup, min_launches: int = 300, min_seconds: float = 0.3):
+    """Run the untimed warm-up: exactly ``warmup`` calls if given; otherwise
+    at least ``min_launches`` calls and at least ``min_seconds`` of them
+    (short kernels need more than 300 launches before the clock has ramped
+    up).  Returns the count."""
+    import torch
+    if warmup is not None:
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        return warmup
+    done, t0 = 0, time.perf_counter()
+    while done < min_launches or time.perf_counter() - t0 < min_seconds:
+        for _ in range(10):
+            fn()
+        done += 10
+        torch.cuda.synchronize()
+    return done
+
+
+def _timed_warm(fn, steps: int):
+    """A comparison timing: about 0.3 s of warm-up (at least 10 calls), then
+    ``steps`` timed calls; ms per call."""
+    _warm_up(fn, None, min_launches=10)
+    return _timed(fn, steps, 0)
 
 
 def _lscpu_model() -> str:
@@ -333,7 +362,8 @@ def rows_main(args) -> int:
           "normalize-bwd": "normalize_backward"}[args.rows]
     nbytes = row_bytes(op, rows, width)
     torch.cuda.synchronize()
-    ms = _timed(step, args.steps, args.warmup)
+    args.warmup = _warm_up(step, args.warmup)
+    ms = _timed(step, args.steps, 0)
     value = nbytes / (ms * 1e-3) / 1e9
 
     parity = cpu = None
@@ -365,7 +395,8 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed launches before timing (default: at least 300 and at least 0.3 s)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--algo", default="auto",
                     choices=["auto", "mfma", "mfma256", "mfma128", "mfma64", "fma", "tiled", "naive", "bf16",
@@ -477,7 +508,8 @@ def main(argv=None) -> int:
 
     flops = w.flops
     torch.cuda.synchronize()
-    ms = _timed(step, args.steps, args.warmup)
+    args.warmup = _warm_up(step, args.warmup)
+    ms = _timed(step, args.steps, 0)
     value = flops / (ms * 1e-3) / 1e12
 
     c_host = dC.cpu().numpy()
@@ -505,7 +537,7 @@ def main(argv=None) -> int:
         ta = view(dA.reshape(-1, A.shape[-1]), *w.a_dims, w.lda_, w.stride_a, w.transA)
         tb = view(dB.reshape(-1, B.shape[-1]), *w.b_dims, w.ldb_, w.stride_b, w.transB)
         out = torch.empty((w.batch, w.M, w.N), dtype=torch.float32, device="cuda")
-        tms = _timed(lambda: torch.bmm(ta, tb, out=out), 10, 2)
+        tms = _timed_warm(lambda: torch.bmm(ta, tb, out=out), 20)
         context = {"torch.bmm (contiguous copies)": {"tflops": flops / (tms * 1e-3) / 1e12,
                                                      "ms": tms}}
     elif not args.no_context and fused:
@@ -519,22 +551,22 @@ def main(argv=None) -> int:
             torch.addmm(dbias, ta, tb, out=out)
             if act == g.ACT_GELU:
                 torch.nn.functional.gelu(out)
-        tms = _timed(unfused, 50, 20)
-        plain = _timed(lambda: g.gemm_f32_ex(
+        tms = _timed_warm(unfused, 50)
+        plain = _timed_warm(lambda: g.gemm_f32_ex(
             w.M, w.N, w.K, dA.data_ptr(), w.lda_, dB.data_ptr(), w.ldb_, dC.data_ptr(), w.ldc_,
-            w.transA, w.transB, stream.cuda_stream, g.ALGOS["mfma"]), 50, 20)
+            w.transA, w.transB, stream.cuda_stream, g.ALGOS["mfma"]), 50)
         context = {"torch addmm+gelu (unfused)": {"tflops": flops / (tms * 1e-3) / 1e12,
                                                   "ms": tms},
                    "gemm_f32 without epilogue": {"tflops": flops / (plain * 1e-3) / 1e12,
                                                  "ms": plain}}
     elif not args.no_context and splitk:
-        plain = _timed(lambda: step(g.ALGOS["mfma"], plain=True), 50, 20)
+        plain = _timed_warm(lambda: step(g.ALGOS["mfma"], plain=True), 50)
         ta = dA[:, :w.a_dims[1]]
         tb = dB[:, :w.b_dims[1]]
         ta = ta.t() if w.transA else ta
         tb = tb.t() if w.transB else tb
         out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
-        tms = _timed(lambda: torch.mm(ta, tb, out=out), 50, 20)
+        tms = _timed_warm(lambda: torch.mm(ta, tb, out=out), 50)
         context = {"gemm_f32 (one product)": {"tflops": flops / (plain * 1e-3) / 1e12, "ms": plain},
                    "torch.mm": {"tflops": flops / (tms * 1e-3) / 1e12, "ms": tms},
                    "workspace_bytes": ws_bytes}
@@ -543,9 +575,9 @@ def main(argv=None) -> int:
         ha, hb = ta.to(torch.bfloat16), tb.to(torch.bfloat16)
         out16 = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
         out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
-        t16 = _timed(lambda: torch.mm(ha, hb, out=out16), 20, 5)
-        t32 = _timed(lambda: torch.mm(ta, tb, out=out), 20, 5)
-        mine = _timed(lambda: step(g.ALGOS["mfma"]), 20, 5)
+        t16 = _timed_warm(lambda: torch.mm(ha, hb, out=out16), 20)
+        t32 = _timed_warm(lambda: torch.mm(ta, tb, out=out), 20)
+        mine = _timed_warm(lambda: step(g.ALGOS["mfma"]), 20)
         context = {"torch.mm bf16 (operands pre-converted, bf16 output)":
                    {"tflops": flops / (t16 * 1e-3) / 1e12, "ms": t16},
                    "torch.mm f32": {"tflops": flops / (t32 * 1e-3) / 1e12, "ms": t32},
@@ -553,9 +585,9 @@ def main(argv=None) -> int:
         if packed:
             # the packing kernels (HBM-bound: 4 bytes read, 2 written per
             # element) and the fused one-step entry point on the same inputs
-            tpa = _timed(lambda: g.pack_bf16(op_a, out=pa), 20, 5)
-            tpb = _timed(lambda: g.pack_bf16(op_b.t(), out=pb), 20, 5)
-            fused1 = _timed(lambda: step(algo_id, plain=True), 20, 5)
+            tpa = _timed_warm(lambda: g.pack_bf16(op_a, out=pa), 20)
+            tpb = _timed_warm(lambda: g.pack_bf16(op_b.t(), out=pb), 20)
+            fused1 = _timed_warm(lambda: step(algo_id, plain=True), 20)
             pbytes = 6 * (w.M * w.K + w.N * w.K)
             context.update({
                 "pack A and B (gemm_f32_pack_bf16)": {"ms": tpa + tpb, "gbps": pbytes / ((tpa + tpb) * 1e-3) / 1e9},
@@ -569,7 +601,9 @@ def main(argv=None) -> int:
             if other == args.algo or (other == "mfma" and args.algo == "auto"):
                 continue
             reps = 3 if other == "naive" else 10
-            oms = _timed(lambda: step(g.ALGOS[other]), reps, 1)
+            # the naive kernel takes tens of ms at full size: warm up by count
+            oms = (_timed(lambda: step(g.ALGOS[other]), reps, 1) if other == "naive"
+                   else _timed_warm(lambda: step(g.ALGOS[other]), reps))
             entry = {"tflops": flops / (oms * 1e-3) / 1e12, "ms": oms}
             if other == "naive":
                 gbps = naive_model_bytes(w.M, w.N, w.K) / (oms * 1e-3) / 1e9
@@ -583,7 +617,7 @@ def main(argv=None) -> int:
         ta = ta.t() if w.transA else ta
         tb = tb.t() if w.transB else tb
         out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
-        tms = _timed(lambda: torch.mm(ta, tb, out=out), 10, 2)
+        tms = _timed_warm(lambda: torch.mm(ta, tb, out=out), 20)
         context["torch.mm"] = {"tflops": flops / (tms * 1e-3) / 1e12, "ms": tms}
 
     # The CPU-baseline leg, the only place this script runs the oracle: the

@@ -93,7 +93,9 @@ constexpr int kBlk = 32;  // MFMA output block edge
 // slices are summed through LDS at the end.  It gives small grids more
 // waves per SIMD without any memory outside the output.  NBUF stage
 // buffers let the copy of stage s + NBUF - 1 run while stage s is computed;
-// FOLD stages form one accumulation chunk on that path.  PREFETCH reads the
+// FOLD stages form one accumulation chunk on that path (0: no chunks, one
+// running accumulator; only the unchunked ablation builds use it, since it
+// does not meet the 1e-6 relative error bound at K = 4096).  PREFETCH reads the
 // LDS fragments of the next k group before the current group's MFMAs
 // (faster with one k-slice; slower when two slices already interleave).
 template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int WPE_, int GROUP_M_,
@@ -119,7 +121,7 @@ struct Config {
     static_assert(BK % 8 == 0, "stages are whole 8-k fragment groups");
     static_assert((BK / 8) % KSPLIT_ == 0, "k-slices share a stage's groups evenly");
     static_assert(KSPLIT_ == 1 || KSPLIT_ == 2 || KSPLIT_ == 4, "k-slices reduce as a binary tree");
-    static_assert(NBUF_ >= 2 && NBUF_ <= 4 && (NBUF_ % FOLD_ == 0 || FOLD_ % NBUF_ == 0),
+    static_assert(NBUF_ >= 2 && NBUF_ <= 4 && (FOLD_ == 0 || NBUF_ % FOLD_ == 0 || FOLD_ % NBUF_ == 0),
                   "2-4 stage buffers; a chunk divides, or is a multiple of, the buffer cycle");
     static_assert(KSPLIT_ == 1 || BM * BN <= (BM + BN) * BK,
                   "a k-slice's partial tile fits in one stage buffer for the reduction");
@@ -298,14 +300,17 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     // buffer it writes was last read in the previous stage, which every wave
     // finished before that stage's barrier).
     constexpr int CH = Cfg::chains;
-    v16f part[CH][FM][FN];
+    constexpr bool kChunked = Cfg::fold > 0;
+    v16f part[kChunked ? CH : 1][kChunked ? FM : 1][kChunked ? FN : 1];
     auto fold_part = [&] {
+        if constexpr (kChunked) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c)
+            for (int c = 0; c < CH; ++c)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] += part[c][i][j];
+                    for (int j = 0; j < FN; ++j) acc[i][j] += part[c][i][j];
+        }
     };
     // MFMAs over the BK k values in `lds` into the partial tile; FRESH starts
     // a chunk (the first MFMA of each chain takes a zero addend), FOLD ends
@@ -344,10 +349,11 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        v16f &p = part[u % CH][i][j];
+                        v16f &p = kChunked ? part[kChunked ? u % CH : 0][kChunked ? i : 0][kChunked ? j : 0]
+                                           : acc[i][j];
                         p = __builtin_amdgcn_mfma_f32_32x32x2f32(
                             fa[cur][i][u], fb[cur][j][u],
-                            (kFresh && t == 0 && u < CH) ? v16f{0.0f} : p, 0, 0, 0);
+                            (kChunked && kFresh && t == 0 && u < CH) ? v16f{0.0f} : p, 0, 0, 0);
                     }
             // With prefetch, ask the scheduler to spread the next group's LDS
             // reads between this group's MFMAs (one read, then an even share
@@ -411,7 +417,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         const char *gb = reinterpret_cast<const char *>(B + int64_t(b_r(0)) * ldb + b_c(0));
         const int64_t a_step = 4 * (A_KC ? int64_t(BK) : int64_t(BK) * lda);
         const int64_t b_step = 4 * (B_KC ? int64_t(BK) : int64_t(BK) * ldb);
-        constexpr int NB = Cfg::nbuf, FOLD = Cfg::fold;
+        constexpr int NB = Cfg::nbuf, FOLD = Cfg::fold > 0 ? Cfg::fold : 1;
         // Copies per wave per stage; every wave issues the same number, so a
         // count of outstanding copies names a stage.
         constexpr int D = TA::dma_per_wave + TB::dma_per_wave;
@@ -538,7 +544,10 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 4, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_CONFIG
-#define GEMM_MFMA_SMALL_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4, 0
+#define GEMM_MFMA_SMALL_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 2, 2, 0
+#endif
+#ifndef GEMM_MFMA_SMALL_DEEP_CONFIG
+#define GEMM_MFMA_SMALL_DEEP_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4, 0
 #endif
 #ifndef GEMM_MFMA_HUGE_CONFIG
 #define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 8, 3, 1, 1, 3, 6, 1
@@ -547,7 +556,16 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1
 #endif
 using Default = Config<GEMM_MFMA_CONFIG>;
+// 64 x 64 tile, two k-slices of 4 waves, 64-k stages in two buffers,
+// 128-k accumulation chunks: a stage long enough to hide one stage of copy
+// latency with half the barriers of 32-k stages, for grids of up to a few
+// tiles per CU (1024^3, one tile per CU: 96.3 vs 94.2 TFLOP/s; 64 products
+// of 512 x 64 x 512: 84.9 vs 82.6; three or four 64-k buffers or 128-k
+// stages were slower).  With more tiles per CU (the ragged 2049 x 3071 x 769
+// product: six) co-resident workgroups hide latency and 32-k stages in a
+// four-buffer ring are faster (85.9 vs 83.5): SmallDeep.
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
+using SmallDeep = Config<GEMM_MFMA_SMALL_DEEP_CONFIG>;
 // 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU (three 48 KB
 // stage buffers, two stages of copies in flight, 192-k accumulation chunks).
 // A quarter fewer bytes copied into LDS per flop than the 128 x 128 tile:
@@ -615,6 +633,10 @@ void dispatch_layout(const Problem &p, hipStream_t s)
 // ragged product 81 -> 86; the 1024 x 4096 x 8192 weight gradient, 256
 // large tiles, stays faster on the large tile).  It is also used when more
 // than a quarter of the large tiles' area would fall outside C (e.g. N = 64).
+// Small tiles from which the deeper-ring variant is used (four per CU).
+#ifndef GEMM_MFMA_SMALL_DEEP_FROM
+#define GEMM_MFMA_SMALL_DEEP_FROM 1024
+#endif
 #ifndef GEMM_MFMA_SMALL_BELOW
 #define GEMM_MFMA_SMALL_BELOW 256
 #endif
@@ -648,8 +670,13 @@ hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
         const bool huge = huge_tiles >= GEMM_MFMA_HUGE_FROM && huge_fits && p.K >= kHugeMinK;
         tile = small ? Small::BM : huge ? Huge::BM : Default::BM;
     }
-    if (tile == Small::BM)
-        dispatch_layout<Small>(p, s);
+    if (tile == Small::BM) {
+        const int64_t small_tiles = int64_t(ceil_div(p.M, Small::BM)) * ceil_div(p.N, Small::BN) * p.batch;
+        if (small_tiles >= GEMM_MFMA_SMALL_DEEP_FROM)
+            dispatch_layout<SmallDeep>(p, s);
+        else
+            dispatch_layout<Small>(p, s);
+    }
     else if (tile == Huge::BM)
         dispatch_layout<Huge>(p, s);
     else
