@@ -142,6 +142,25 @@ def _timed(fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps
 
 
+def _timed_windows(fn, steps: int, windows: int = 3):
+    """The timed region: exactly ``steps`` calls between two synchronisations,
+    with HIP events also splitting them into ``windows`` consecutive windows.
+    Returns (ms per call over all steps, [ms per call in each window])."""
+    import torch
+    torch.cuda.synchronize()
+    bounds = [round(i * steps / windows) for i in range(windows + 1)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    events[0].record()
+    for w in range(windows):
+        for _ in range(bounds[w + 1] - bounds[w]):
+            fn()
+        events[w + 1].record()
+    torch.cuda.synchronize()
+    per = [events[w].elapsed_time(events[w + 1]) / max(bounds[w + 1] - bounds[w], 1)
+           for w in range(windows)]
+    return events[0].elapsed_time(events[-1]) / steps, per
+
+
 def _warm_up(fn, warmup, min_launches: int = 300, min_seconds: float = 0.3):
     """Run the untimed warm-up: exactly ``warmup`` calls if given; otherwise
     at least ``min_launches`` calls and at least ``min_seconds`` of them
@@ -237,7 +256,15 @@ def cpu_baseline(w, target_s: float = 12.0, mixed: bool = False) -> dict:
     rows = int(min(w.M, max(probe_rows, target_s / max(t_probe, 1e-9) * probe_rows)))
     t = run(rows)
     tflops = gemm_flops(rows, w.N, w.K) / t / 1e12
+    # context: numpy's float64 product (the host BLAS) on the same panel
+    a64 = np.ascontiguousarray(A[:, :rows].T if w.transA else A[:rows], dtype=np.float64)[:, :w.K]
+    b64 = (B[:w.N, :w.K].T if w.transB else B[:w.K, :w.N]).astype(np.float64)
+    t0 = time.perf_counter()
+    a64 @ b64
+    t_np = time.perf_counter() - t0
     return {"value": tflops, "unit": "TFLOPS", "cores": orc.threads(), "kind": "oracle",
+            "numpy_f64_matmul_same_panel": {"tflops": gemm_flops(rows, w.N, w.K) / t_np / 1e12,
+                                            "seconds": t_np, "note": "context, not the oracle"},
             "sample": f"first {rows} of {w.M} rows of C ({w.name}: {w.M}x{w.N}x{w.K}), "
                       f"{t:.1f} s, FP64-accumulating triple loop"
                       f"{' on bf16-rounded operands' if mixed else ''}, OpenMP over rows",
@@ -375,7 +402,7 @@ def rows_main(args) -> int:
     nbytes = row_bytes(op, rows, width)
     torch.cuda.synchronize()
     args.warmup = _warm_up(step, args.warmup)
-    ms = _timed(step, args.steps, 0)
+    ms, windows = _timed_windows(step, args.steps)
     value = nbytes / (ms * 1e-3) / 1e9
 
     parity = cpu = None
@@ -385,7 +412,7 @@ def rows_main(args) -> int:
     line = {
         "metric": f"row reduction HBM throughput ({op}, algorithmic bytes / s)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": ms, "windows_ms_per_step": windows, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.rows, "rows": rows, "width": width,
                    "scale": scale if "softmax" in op else None, "eps": eps if "normalize" in op else None,
@@ -521,7 +548,7 @@ def main(argv=None) -> int:
     flops = w.flops
     torch.cuda.synchronize()
     args.warmup = _warm_up(step, args.warmup)
-    ms = _timed(step, args.steps, 0)
+    ms, windows = _timed_windows(step, args.steps)
     value = flops / (ms * 1e-3) / 1e12
 
     c_host = dC.cpu().numpy()
@@ -661,6 +688,7 @@ def main(argv=None) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "windows_ms_per_step": windows,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
