@@ -98,13 +98,16 @@ constexpr int kBlk = 32;  // MFMA output block edge
 // does not meet the 1e-6 relative error bound at K = 4096).  PREFETCH reads the
 // LDS fragments of the next k group before the current group's MFMAs
 // (faster with one k-slice; slower when two slices already interleave).
+// PRIO raises a wave's issue priority while it issues its MFMAs, so that
+// waves feeding the matrix core are preferred over waves copying or waiting.
 template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int WPE_, int GROUP_M_,
-          int WRITE_G_, int CHAINS_, int KSPLIT_, int NBUF_, int FOLD_, int PREFETCH_>
+          int WRITE_G_, int CHAINS_, int KSPLIT_, int NBUF_, int FOLD_, int PREFETCH_, int PRIO_ = 0>
 struct Config {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int nbuf = NBUF_;  // LDS stage buffers (copies in flight: NBUF - 1)
     static constexpr int fold = FOLD_;  // stages per accumulation chunk on the copy path
     static constexpr bool prefetch = PREFETCH_;  // read k group t + 1 before group t's MFMAs
+    static constexpr bool prio = PRIO_;          // raised issue priority while issuing MFMAs
     static constexpr int ksplit = KSPLIT_;                 // k-slices of waves
     static constexpr int waves_mn = WAVES_M * WAVES_N;     // waves per k-slice
     static constexpr int waves = waves_mn * KSPLIT_;
@@ -335,6 +338,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             for (int j = 0; j < FN; ++j) fb[slot][j] = TB::fragment(lb, wn + j * kBlk + l32, g, half);
         };
         if (Cfg::prefetch) read(0, 0);
+        if constexpr (Cfg::prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < kGroups; ++t) {
             const int cur = Cfg::prefetch ? (t & 1) : 0;
@@ -370,6 +374,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                 if (kMfma > per * kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - per * kReads, 0);
             }
         }
+        if constexpr (Cfg::prio) __builtin_amdgcn_s_setprio(0);
         if (Cfg::ksplit > 1 || Cfg::write_g >= kGroups) mid();
         if (kFold) fold_part();
     };
@@ -544,7 +549,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 4, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_CONFIG
-#define GEMM_MFMA_SMALL_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 2, 2, 0
+#define GEMM_MFMA_SMALL_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 2, 2, 0, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_DEEP_CONFIG
 #define GEMM_MFMA_SMALL_DEEP_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4, 0
@@ -553,17 +558,18 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 8, 3, 1, 1, 3, 6, 1
 #endif
 #ifndef GEMM_MFMA_KK_CONFIG
-#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1
+#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1, 1
 #endif
 using Default = Config<GEMM_MFMA_CONFIG>;
 // 64 x 64 tile, two k-slices of 4 waves, 64-k stages in two buffers,
 // 128-k accumulation chunks: a stage long enough to hide one stage of copy
 // latency with half the barriers of 32-k stages, for grids of up to a few
 // tiles per CU (1024^3, one tile per CU: 96.3 vs 94.2 TFLOP/s; 64 products
-// of 512 x 64 x 512: 84.9 vs 82.6; three or four 64-k buffers or 128-k
-// stages were slower).  With more tiles per CU (the ragged 2049 x 3071 x 769
-// product: six) co-resident workgroups hide latency and 32-k stages in a
-// four-buffer ring are faster (85.9 vs 83.5): SmallDeep.
+// of 512 x 64 x 512: 84.9 vs 82.6, and 85.6 vs 83.9 with raised MFMA issue
+// priority; three or four 64-k buffers or 128-k stages were slower).  With
+// more tiles per CU (the ragged 2049 x 3071 x 769 product: six) co-resident
+// workgroups hide latency and 32-k stages in a four-buffer ring are faster
+// (85.9 vs 83.5): SmallDeep.
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
 using SmallDeep = Config<GEMM_MFMA_SMALL_DEEP_CONFIG>;
 // 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU (three 48 KB
@@ -574,7 +580,8 @@ using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // Large tile when both operands are k-contiguous (A untransposed, B
 // transposed): every DMA row segment is a short run along k, and four
 // 16-k stage buffers in flight hide its latency better (the
-// 8192 x 1024 x 4096 input-gradient product: 125 -> 129 TFLOP/s).
+// 8192 x 1024 x 4096 input-gradient product: 125 -> 129 TFLOP/s; with
+// raised MFMA issue priority 131.1 -> 135.1).
 using DefaultKK = Config<GEMM_MFMA_KK_CONFIG>;
 
 // True if every DMA offset of an operand's stage fits in 32 bits.
