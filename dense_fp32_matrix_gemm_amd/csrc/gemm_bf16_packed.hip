@@ -27,10 +27,10 @@
 //  * Interior tiles copy full stages by DMA, NBUF - 1 stages ahead, one
 //    barrier per stage; edge tiles and a partial last stage go through
 //    registers with every element predicated (zero outside the matrix).
-//  * The large tile keeps one accumulator: each MFMA adds 16 exact products
-//    before it rounds, so the relative error of a K = 8192 product stays
-//    near 5e-7.  The small tile, used past K = 16384, sums runs of FOLD
-//    stages into a fresh partial first.
+//  * The 256 x 256 and 256 x 128 tiles keep one accumulator: each MFMA adds
+//    16 exact products before it rounds, so the relative error of a K = 8192
+//    product stays near 5e-7.  The 128 x 128 tile, also used past K = 16384,
+//    sums runs of FOLD stages into a fresh partial first.
 #include "tile_common.hpp"
 
 namespace gemmf32 {

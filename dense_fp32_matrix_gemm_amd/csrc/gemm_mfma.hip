@@ -11,14 +11,18 @@
 //    product done by the matrix core: one v_mfma_f32_32x32x2_f32 is a rank-2
 //    update of a 32 x 32 block, 4096 flops per wave instruction).  At about
 //    128 registers per lane, two workgroups (16 waves) share a CU, four
-//    waves per SIMD to hide LDS and barrier latency.
-//  * Staging, interior tiles: each K stage (BK = 32) is copied from global
-//    memory straight into LDS with global_load_lds_dwordx4 (each wave
-//    instruction moves 64 x 16 bytes; no registers, no LDS write
-//    instructions), issued one stage ahead into the other of two LDS
-//    buffers, so one barrier per stage suffices (the double buffering of the
-//    cuda-oxide book's summary; the page's second barrier is not needed
-//    because the buffer being filled is never the one being read).
+//    waves per SIMD to hide LDS and barrier latency.  Large grids with long
+//    k take a 256 x 128 tile (one workgroup per CU), small grids a 64 x 64
+//    tile whose k groups are split over two slices of waves; the
+//    configurations and where each is used are listed below the kernel.
+//  * Staging, interior tiles: each K stage (BK = 32; 16 or 64 in some
+//    configurations) is copied from global memory straight into LDS with
+//    global_load_lds_dwordx4 (each wave instruction moves 64 x 16 bytes; no
+//    registers, no LDS write instructions), issued one or more stages ahead
+//    into another LDS buffer, so one barrier per stage suffices (the double
+//    buffering of the cuda-oxide book's summary; the page's second barrier
+//    is not needed because the buffer being filled is never the one being
+//    read).
 //  * Staging, edge tiles and the last partial stage: 16-byte (or scalar)
 //    loads into registers with every element predicated, zero outside the
 //    matrix (section 3.3's kernel assumes tile multiples), written to LDS
