@@ -76,8 +76,12 @@ __device__ __forceinline__ void wait_vm()
 // BM x BN of C per workgroup, BK bf16 per stage, WAVES_M x WAVES_N waves,
 // NBUF LDS stage buffers (copies in flight: NBUF - 1), GROUP_M tile-rows per
 // group of the launch order, FOLD stages per accumulation chunk (0: one
-// running accumulator).
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int NBUF_, int GROUP_M_, int FOLD_>
+// running accumulator), STAGGER: the second half of the waves issues its
+// share of the next stage's copies after the first MFMA step instead of
+// right after the barrier, so the two waves of a SIMD do not both stall on
+// copy issue at once.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int NBUF_, int GROUP_M_, int FOLD_,
+          int STAGGER_ = 0>
 struct Config {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int waves_n = WAVES_N_;
@@ -86,6 +90,7 @@ struct Config {
     static constexpr int WM = BM / WAVES_M_, WN = BN / WAVES_N_;
     static constexpr int FM = WM / kBlk, FN = WN / kBlk;
     static constexpr int nbuf = NBUF_, group_m = GROUP_M_, fold = FOLD_;
+    static constexpr bool stagger = STAGGER_;
     static_assert(WM % kBlk == 0 && WN % kBlk == 0, "wave tiles are whole MFMA blocks");
     static_assert(BK == 32 || BK == 64, "a stage row is 4 or 8 16-byte vectors");
     static_assert(NBUF_ >= 2 && NBUF_ <= 4, "2-4 stage buffers");
@@ -219,7 +224,8 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
     // Products over the BK k values in `lds`.  Unchunked: straight into acc.
     // Chunked: into the partial tile, which FRESH starts from zero and FOLD
     // adds into acc.
-    auto compute = [&](const char *lds, auto fresh_t, auto fold_t) {
+    // `after_step0` runs once, after the MFMAs of the first step.
+    auto compute = [&](const char *lds, auto fresh_t, auto fold_t, auto after_step0) {
         constexpr bool kFresh = decltype(fresh_t)::value;
         constexpr bool kFold = decltype(fold_t)::value;
         const char *la = lds;
@@ -253,6 +259,7 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
                                                                            acc[i][j], 0, 0, 0);
                     }
                 }
+            if (g == 0) after_step0();
             // Spread the next step's LDS reads between this step's MFMAs.
             if (g + 1 < kSteps) {
                 constexpr int kReads = FM + FN, kMfma = FM * FN;
@@ -310,9 +317,15 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
                     else
                         wait_vm<(NB - 2) * D>();
                     __syncthreads();
-                    if (st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
+                    // Copies are counted per wave in issue order, so a wave
+                    // that copies after the first step still has the same
+                    // count outstanding at the next wait.
+                    const bool late = Cfg::stagger && wave >= Cfg::waves / 2;
+                    if (!late && st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
                     constexpr int F = FOLD > 0 ? FOLD : 1;
-                    compute(bufp(Int<b % NB>{}), Bool<b % F == 0>{}, Bool<b % F == F - 1>{});
+                    compute(bufp(Int<b % NB>{}), Bool<b % F == 0>{}, Bool<b % F == F - 1>{}, [&] {
+                        if (late && st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
+                    });
                 }
             });
         }
@@ -330,7 +343,7 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
             TA::store(buf0, ra);
             TB::store(buf0 + TA::bytes, rb);
             __syncthreads();
-            compute(buf0, Bool<true>{}, Bool<true>{});
+            compute(buf0, Bool<true>{}, Bool<true>{}, [] {});
         }
     } else {
         // Register-staged: stage s + 1 is loaded while stage s is computed,
@@ -349,7 +362,7 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
                 TA::template load<VEC>(A, lda, M, K, m0, (s + 1) * BK, ra);
                 TB::template load<VEC>(B, ldb, N, K, n0, (s + 1) * BK, rb);
             }
-            compute(cur, Bool<true>{}, Bool<true>{});
+            compute(cur, Bool<true>{}, Bool<true>{}, [] {});
             if (s + 1 < stages) {
                 TA::store(nxt, ra);
                 TB::store(nxt + TA::bytes, rb);
@@ -383,14 +396,14 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
 // than the deeper ring).  Mid: 256 x 128, 8 waves of 64 x 64, otherwise the
 // same (96 KB), for grids with fewer large tiles than CUs (8192 x 1024 x
 // 4096: 900 vs 750 TFLOP/s on the small tile, whose 32-k stages it also
-// beats).  Small: 128 x 128, 8 waves of 32 x 64, 32-k stages
+// beats), with staggered copies (+3 % there; neutral on the 256 x 256 tile).  Small: 128 x 128, 8 waves of 32 x 64, 32-k stages
 // in a four-buffer ring, runs of 128 k summed into a fresh partial first
 // (about 100 registers, so two workgroups share a CU).
 #ifndef GEMM_PACKED_LARGE_CONFIG
 #define GEMM_PACKED_LARGE_CONFIG 256, 256, 64, 4, 2, 2, 4, 0
 #endif
 #ifndef GEMM_PACKED_MID_CONFIG
-#define GEMM_PACKED_MID_CONFIG 256, 128, 64, 4, 2, 2, 4, 0
+#define GEMM_PACKED_MID_CONFIG 256, 128, 64, 4, 2, 2, 4, 0, 1
 #endif
 #ifndef GEMM_PACKED_SMALL_CONFIG
 #define GEMM_PACKED_SMALL_CONFIG 128, 128, 32, 4, 2, 4, 8, 4
