@@ -81,7 +81,7 @@ def compulsory_bytes(M: int, N: int, K: int) -> int:
 # The sources each kernel family is compiled from (its own file plus the
 # shared headers); a counter summary stays valid while these are unchanged.
 KERNEL_SOURCES = {
-    "gemm_f32_mfma": ["gemm_mfma.hip", "tile_common.hpp", "gemm_internal.hpp"],
+    "gemm_f32_mfma": ["gemm_mfma.hip", "gemm_mfma_wide.hip", "tile_common.hpp", "gemm_internal.hpp"],
     "gemm_f32_fma": ["gemm_fma.hip", "tile_common.hpp", "gemm_internal.hpp"],
     "gemm_f32_tiled": ["gemm_simple.hip", "gemm_internal.hpp"],
     "gemm_f32_naive": ["gemm_simple.hip", "gemm_internal.hpp"],
@@ -438,7 +438,7 @@ def main(argv=None) -> int:
                     help="untimed launches before timing (default: at least 300 and at least 0.3 s)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--algo", default="auto",
-                    choices=["auto", "mfma", "mfma256", "mfma128", "mfma64", "fma", "tiled", "naive", "bf16",
+                    choices=["auto", "mfma", "mfma256", "mfma128", "mfma64", "mfmawide", "fma", "tiled", "naive", "bf16",
                              "bf16packed"],
                     help="kernel family; bf16 times the mixed-precision entry point "
                          "(operands rounded to bf16, FP32 sums), bf16packed its two-step form "
@@ -553,7 +553,8 @@ def main(argv=None) -> int:
 
     c_host = dC.cpu().numpy()
 
-    kernel = "gemm_f32_" + ("mfma" if args.algo in ("auto", "mfma256", "mfma128", "mfma64") else args.algo)
+    kernel = "gemm_f32_" + ("mfma" if args.algo in ("auto", "mfma256", "mfma128", "mfma64", "mfmawide")
+                            else args.algo)
     peak = MI355X_BF16_PEAK_TFLOPS if mixed else MI355X_FP32_PEAK_TFLOPS
     roofline = {"bound": "mfma", "achieved": value, "peak": peak,
                 "unit": "TFLOP/s", "frac": value / peak,

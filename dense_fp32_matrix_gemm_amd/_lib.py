@@ -15,10 +15,10 @@ import threading
 from . import build as _build
 
 ALGO_AUTO, ALGO_MFMA, ALGO_FMA, ALGO_TILED, ALGO_NAIVE = 0, 1, 2, 3, 4
-ALGO_MFMA_TILE128, ALGO_MFMA_TILE64, ALGO_MFMA_TILE256 = 5, 6, 7
+ALGO_MFMA_TILE128, ALGO_MFMA_TILE64, ALGO_MFMA_TILE256, ALGO_MFMA_WIDE = 5, 6, 7, 8
 ALGOS = {"auto": ALGO_AUTO, "mfma": ALGO_MFMA, "fma": ALGO_FMA, "tiled": ALGO_TILED,
          "naive": ALGO_NAIVE, "mfma128": ALGO_MFMA_TILE128, "mfma64": ALGO_MFMA_TILE64,
-         "mfma256": ALGO_MFMA_TILE256}
+         "mfma256": ALGO_MFMA_TILE256, "mfmawide": ALGO_MFMA_WIDE}
 
 # Every symbol include/gemm_f32.h declares, with (restype, argtypes).
 _i64, _ptr, _int, _flt = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float

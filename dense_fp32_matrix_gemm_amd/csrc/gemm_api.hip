@@ -61,10 +61,13 @@ int run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
 {
     const int bad = validate(M, N, K, A, lda, B, ldb, C, ldc, transA, transB);
     if (bad) return bad;
-    if (algo < GEMM_F32_ALGO_AUTO || algo > GEMM_F32_ALGO_MFMA_TILE256) return -kArgAlgo;
+    if (algo < GEMM_F32_ALGO_AUTO || algo > GEMM_F32_ALGO_MFMA_WIDE) return -kArgAlgo;
+    const Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
+    // The 256 x 256 kernel runs only the problems in its domain.
+    if (algo == GEMM_F32_ALGO_MFMA_WIDE && M > 0 && N > 0 && K > 0 && !gemmf32::mfma_wide_fits(p))
+        return -kArgAlgo;
     if (M == 0 || N == 0) return 0;  // nothing to write
 
-    const Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     if (K == 0) {
@@ -77,6 +80,7 @@ int run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
         case GEMM_F32_ALGO_MFMA_TILE128: err = gemmf32::launch_mfma(p, s, 128); break;
         case GEMM_F32_ALGO_MFMA_TILE64: err = gemmf32::launch_mfma(p, s, 64); break;
         case GEMM_F32_ALGO_MFMA_TILE256: err = gemmf32::launch_mfma(p, s, 256); break;
+        case GEMM_F32_ALGO_MFMA_WIDE: err = gemmf32::launch_mfma_wide(p, s); break;
         case GEMM_F32_ALGO_MFMA:
         case GEMM_F32_ALGO_AUTO:
         default: err = gemmf32::launch_mfma(p, s, 0); break;
@@ -300,6 +304,6 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda
     return err == hipSuccess ? 0 : int(err);
 }
 
-int gemm_f32_version(void) { return 10500; }
+int gemm_f32_version(void) { return 10600; }
 
 }  // extern "C"

@@ -38,8 +38,18 @@ struct Problem {
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_tiled(const Problem &p, hipStream_t stream);
 hipError_t launch_fma(const Problem &p, hipStream_t stream);
-// tile: 0 chooses by problem size; 256 (256 x 128), 128 or 64 forces that tile.
+// tile: 0 chooses by problem size (the 256 x 256 kernel when it is preferred);
+// 256 (256 x 128), 128 or 64 forces that tile.
 hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
+// The 256 x 256 MFMA kernel with one running sum per output
+// (gemm_mfma_wide.hip).  fits: the problem is in its domain (operands
+// untransposed, M and N multiples of 256, K a multiple of 32 and at most
+// 1024, 16-byte aligned operands and strides, no split k).  preferred: it
+// fits and has at least one tile per CU; launch_mfma with tile 0 then takes
+// it.  The launcher assumes fits.
+bool mfma_wide_fits(const Problem &p);
+bool mfma_wide_preferred(const Problem &p);
+hipError_t launch_mfma_wide(const Problem &p, hipStream_t stream);
 // tile: 0 chooses by problem size; 256 (256 x 256) or 128 forces that tile.
 // Operands rounded to bf16 (nearest, ties to even), bf16 matrix-core
 // products, FP32 sums and output.  Ignores batch, bias and act.

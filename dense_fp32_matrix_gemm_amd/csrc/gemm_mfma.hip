@@ -690,6 +690,7 @@ constexpr int kHugeMinK = 512;
 
 hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
 {
+    if (tile == 0 && mfma_wide_preferred(p)) return launch_mfma_wide(p, s);
     if (tile == 0) {
         const int64_t big_tiles =
             int64_t(ceil_div(p.M, Default::BM)) * ceil_div(p.N, Default::BN) * p.batch;

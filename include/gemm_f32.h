@@ -43,8 +43,9 @@
  *         invalid: M/N/K < 0 (-1/-2/-3); A NULL while M*K > 0 (-4); lda too
  *         small (-5); B NULL while K*N > 0 (-6); ldb too small (-7); C NULL
  *         while M*N > 0 (-8); ldc too small (-9); transA/transB not 0 or 1
- *         (-10/-11); algo unknown (-13, gemm_f32_ex only); a dimension or
- *         leading dimension >= 2^31 is reported as invalid for that
+ *         (-10/-11); algo unknown, or GEMM_F32_ALGO_MFMA_WIDE for a
+ *         problem outside its domain (-13, gemm_f32_ex only); a dimension
+ *         or leading dimension >= 2^31 is reported as invalid for that
  *         argument.  Validation is done on the host before any HIP call,
  *         so these codes are returned even on a machine without a GPU.
  *    >0   a hipError_t reported by the kernel launch (hipGetLastError()
@@ -71,7 +72,17 @@ enum gemm_f32_algo {
     GEMM_F32_ALGO_NAIVE = 4, /* one lane per output, operands from global memory (3.1) */
     GEMM_F32_ALGO_MFMA_TILE128 = 5, /* MFMA with the 128 x 128 tile forced */
     GEMM_F32_ALGO_MFMA_TILE64 = 6,  /* MFMA with the 64 x 64 (split-k-group) tile forced */
-    GEMM_F32_ALGO_MFMA_TILE256 = 7  /* MFMA with the 256 x 128 tile forced */
+    GEMM_F32_ALGO_MFMA_TILE256 = 7, /* MFMA with the 256 x 128 tile forced */
+    GEMM_F32_ALGO_MFMA_WIDE = 8     /* MFMA with the 256 x 256 tile and one running
+                                       FP32 sum per output (relative error about
+                                       2^-24 * sqrt(K / 12) on zero-mean data, so
+                                       K <= 1024 keeps it below 1e-6).  Only for
+                                       transA = transB = 0, M and N multiples of 256,
+                                       K a multiple of 32 and at most 1024, A and B
+                                       16-byte aligned with lda and ldb multiples of
+                                       4; any other non-empty problem returns -13.
+                                       AUTO takes it for such problems with at least
+                                       256 tiles. */
 };
 
 /* C = op(A) . op(B) on the fastest path (GEMM_F32_ALGO_AUTO). */

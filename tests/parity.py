@@ -18,7 +18,8 @@ import numpy as np
 
 import gemm_inputs as gi
 
-ALGO_IDS = {"auto": 0, "mfma": 1, "fma": 2, "tiled": 3, "naive": 4, "mfma128": 5, "mfma64": 6, "mfma256": 7}
+ALGO_IDS = {"auto": 0, "mfma": 1, "fma": 2, "tiled": 3, "naive": 4, "mfma128": 5, "mfma64": 6, "mfma256": 7,
+            "mfmawide": 8}
 ELEM_ABS, ELEM_REL, FROB_REL = 1e-6, 1e-5, 1e-6
 
 

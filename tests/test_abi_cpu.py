@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert g.gemm_f32_version() == 10500
+    assert g.gemm_f32_version() == 10600
 
 
 def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
@@ -82,8 +82,34 @@ def test_invalid_arguments(fn, kwargs, code):
 
 
 def test_invalid_algo():
-    assert call(fn="gemm_f32_ex", algo=8) == -13
+    assert call(fn="gemm_f32_ex", algo=9) == -13
     assert call(fn="gemm_f32_ex", algo=-1) == -13
+
+
+WIDE = g.ALGOS["mfmawide"]
+ALIGNED = 0x10000  # 16-byte aligned, never dereferenced
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(ta=1), dict(tb=1),                          # transposed operands
+    dict(M=300), dict(N=200),                        # not multiples of 256
+    dict(K=1056), dict(K=40), dict(K=16),            # K above 1024 or not a multiple of 32
+    dict(lda=66), dict(ldb=258),                     # leading dimensions not multiples of 4
+    dict(A=ALIGNED + 4), dict(B=ALIGNED + 8),        # operands not 16-byte aligned
+], ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
+def test_wide_refuses_problems_outside_its_domain(kwargs):
+    """The 256 x 256 kernel runs only untransposed, aligned products with M
+    and N multiples of 256 and K a multiple of 32 up to 1024: anything else
+    is -13, decided on the host before any HIP call."""
+    args = dict(M=256, N=256, K=64, A=ALIGNED, B=ALIGNED, C=ALIGNED)
+    args.update(kwargs)
+    assert call(fn="gemm_f32_ex", algo=WIDE, **args) == -13
+
+
+def test_wide_quick_returns_before_its_domain_check():
+    """Empty outputs return 0 whatever the shape; K == 0 is the zero fill."""
+    assert call(fn="gemm_f32_ex", algo=WIDE, M=0, N=300, K=40, A=None, C=None) == 0
+    assert call(fn="gemm_f32_ex", algo=WIDE, M=300, N=0, K=40, B=None, C=None) == 0
 
 
 @pytest.mark.parametrize("kwargs", [dict(M=0, A=None, C=None), dict(N=0, B=None, C=None),
@@ -134,7 +160,7 @@ def test_operand_layout_from_strides():
 def test_header_is_plain_c():
     """The public header compiles as C with no HIP headers on the include path."""
     import subprocess
-    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10500 ? 0 : 1;}\n"
+    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10600 ? 0 : 1;}\n"
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
                        input=src, capture_output=True, text=True)
