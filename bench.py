@@ -142,6 +142,15 @@ def _timed(fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps
 
 
+def _window_summary(windows, work):
+    """Median and fastest of the timed windows (ms per step), and the rate
+    at each (work per step / time, in the line's unit)."""
+    import statistics
+    med, fast = statistics.median(windows), min(windows)
+    return {"median_ms": med, "min_ms": fast,
+            "value_at_median": work / (med * 1e-3) / 1e12, "value_at_min": work / (fast * 1e-3) / 1e12}
+
+
 def _timed_windows(fn, steps: int, windows: int = 3):
     """The timed region: exactly ``steps`` calls between two synchronisations,
     with HIP events also splitting them into ``windows`` consecutive windows.
@@ -690,6 +699,7 @@ def main(argv=None) -> int:
         "warmup": args.warmup,
         "ms_per_step": ms,
         "windows_ms_per_step": windows,
+        "windows_summary": _window_summary(windows, flops),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
