@@ -151,6 +151,25 @@ def _window_summary(windows, work):
             "value_at_median": work / (med * 1e-3) / 1e12, "value_at_min": work / (fast * 1e-3) / 1e12}
 
 
+def _timed_cold(fn, reps: int = 30, scratch_mb: int = 512):
+    """Mean ms of fn when each launch follows a scratch write larger than the
+    caches; each launch is bracketed by its own HIP events on the current
+    stream (the fills run between them, so the GPU never idles)."""
+    import torch
+    scratch = torch.empty(scratch_mb << 18, dtype=torch.float32, device="cuda")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        scratch.fill_(float(i))
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / reps
+    del scratch
+    return ms
+
+
 def _timed_windows(fn, steps: int, windows: int = 3):
     """The timed region: exactly ``steps`` calls between two synchronisations,
     with HIP events also splitting them into ``windows`` consecutive windows.
@@ -670,6 +689,11 @@ def main(argv=None) -> int:
         tms = _timed_warm(lambda: torch.mm(ta, tb, out=out), 20)
         context["torch.mm"] = {"tflops": flops / (tms * 1e-3) / 1e12, "ms": tms}
         vendor_host = out.cpu().numpy()
+        # cold cache: each launch after a 512 MB scratch write, which evicts
+        # A, B and C from L2 and the 256 MB Infinity Cache
+        cms = _timed_cold(lambda: step(algo_id))
+        context["cold_cache"] = {"tflops": flops / (cms * 1e-3) / 1e12, "ms": cms, "scratch_mb": 512,
+                                 "launches": 30, "note": "each launch timed alone after a 512 MB write"}
 
     # The CPU-baseline leg, the only place this script runs the oracle: the
     # oracle timed on a sample of the workload, and a sampled check of the

@@ -50,6 +50,8 @@ def test_default_line_with_cpu_baseline():
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
     assert d["parity"]["ok"] and d["parity"]["relfrob_3000_sampled"] <= 1e-6
     assert "torch.mm" in d["context"] and "relfrob_3000_sampled" in d["context"]["torch.mm"]
+    cold = d["context"]["cold_cache"]
+    assert cold["tflops"] > 0 and cold["scratch_mb"] == 512
     ws = d["windows_summary"]
     assert len(d["windows_ms_per_step"]) == 3 and ws["min_ms"] <= ws["median_ms"]
     assert ws["value_at_min"] >= ws["value_at_median"] > 0
