@@ -42,8 +42,8 @@ hipError_t launch_fma(const Problem &p, hipStream_t stream);
 // 256 (256 x 128), 128 or 64 forces that tile.
 hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
 // The 256 x 256 MFMA kernel with one running sum per output
-// (gemm_mfma_wide.hip).  fits: the problem is in its domain (operands
-// untransposed, M and N multiples of 256, K a multiple of 32 and at most
+// (gemm_mfma_wide.hip).  fits: the problem is in its domain (any
+// transposes, M and N multiples of 256, K a multiple of 32 and at most
 // 1024, 16-byte aligned operands and strides, no split k).  preferred: it
 // fits and has at least one tile per CU; launch_mfma with tile 0 then takes
 // it.  The launcher assumes fits.

@@ -13,12 +13,11 @@
 //    of a 128 x 128 tile and a third less than 256 x 128.  About 180
 //    registers per lane and two 64 KB stage buffers: one workgroup per CU,
 //    two waves per SIMD.
-//  * Operands untransposed (A's stored rows run along k, B's along n), M and
-//    N multiples of 256, K a multiple of 32, both operands 16-byte aligned
-//    with leading dimensions that are multiples of 4 floats: every tile is
-//    interior and every stage is one DMA copy.  The host checks all of this
-//    (gemm_mfma_wide_fits); other problems go to the kernels of
-//    gemm_mfma.hip.
+//  * Any transposes (one instantiation per layout), M and N multiples of
+//    256, K a multiple of 32, both operands 16-byte aligned with leading
+//    dimensions that are multiples of 4 floats: every tile is interior and
+//    every stage is one DMA copy.  The host checks all of this
+//    (mfma_wide_fits); other problems go to the kernels of gemm_mfma.hip.
 //  * Staging: each 32-k stage is copied global -> LDS with
 //    global_load_lds_dwordx4 one stage ahead into the other buffer (one
 //    barrier per stage).  The buffer is picked at run time from the stage
@@ -27,7 +26,7 @@
 //  * Fragments: the k order inside a group of 8 k values is the one of
 //    gemm_mfma.hip (lanes 0-31 take k = u, lanes 32-63 k = 4 + u for the
 //    four MFMAs u of the group).  The fragments of group g + 1 are read while
-//    group g's 32 MFMAs run, interleaved one LDS read per three MFMAs.
+//    group g's 32 MFMAs run, the LDS reads spread evenly between them.
 //  * Accumulation: one running sum per output.  The matrix core rounds once
 //    per MFMA (two products), so for zero-mean data the relative error grows
 //    like u * sqrt(K / 12) (u = 2^-24): 5.7e-7 at K = 1024, which is why
@@ -45,8 +44,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
 constexpr int kFM = 2, kFN = 4;        // 32 x 32 blocks per wave: 64 x 128
-constexpr int kAVec = kBK / 4;         // A stage: 256 rows (m) of 8 vectors (k)
-constexpr int kBVec = kBN / 4;         // B stage: 32 rows (k) of 64 vectors (n)
+constexpr int kP = 256;                // extent of each operand's tile along m or n
+static_assert(kBM == kP && kBN == kP, "both operands' tiles are 256 x 32");
 constexpr int kAFloats = kBM * kBK, kBFloats = kBK * kBN;
 constexpr int kStage = kAFloats + kBFloats;        // 16384 floats = 64 KB
 constexpr int kAPieces = kAFloats / 256 / kWaves;  // 1 KB copies per wave per stage
@@ -57,15 +56,68 @@ constexpr int kWideMinTiles = 256;  // auto selection: at least one tile per CU
 static_assert(kAPieces * kWaves * 256 == kAFloats && kBPieces * kWaves * 256 == kBFloats,
               "each stage splits into whole 1 KB copies per wave");
 
-// 16-byte vector v of an A row r (8 vectors) sits in slot v ^ swz_a(r); of a
-// B row r (64 vectors) in slot v ^ swz_b(r).  A fragment read takes row
-// wm + 32 i + l32 and vector 2 g + half: the XOR spreads the 32 rows of a
-// half-wave over all eight slots.  A B fragment read takes 32 consecutive
-// floats of row k from lanes 0-31 and of row k + 4 from lanes 32-63; rows
-// with bit 2 of k set are shifted by 8 vectors (32 floats), so the two
-// halves of the wave hit disjoint banks.
-__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_b(int r) { return ((r >> 2) & 1) << 3; }
+// One operand's stage tile in LDS: the 256 rows (or columns) of C it feeds
+// times 32 k, in one of two layouts.
+//
+// KC (the stored rows run along k: A untransposed, B transposed): 256 rows
+// of 8 16-byte vectors; vector v of row r sits in slot v ^ swz(r).  A
+// fragment read takes row p + l32 and vector 2 g + half, one 16-byte LDS
+// read per lane; the XOR spreads the 32 rows of a half-wave over all eight
+// slots.  Block b (32 rows further) is 32 * 32 floats further.
+//
+// Not KC (the stored rows run along m or n): 32 rows (k) of 64 vectors;
+// rows with bit 2 of k set have their vectors shifted by 8 (32 floats), so
+// lanes 0-31, reading 32 consecutive floats of row k, and lanes 32-63,
+// reading row k + 4, hit disjoint banks.  A fragment is four rows k .. k + 3
+// of column p + 32 b + l32 with k = 8 g + 4 half.  For p a multiple of 64
+// and b < 4, the column's vector index has bits 3-4 equal to b and the
+// shift flips bit 3 exactly when half = 1, so block b of this lane sits at
+// float p + l32 + 32 * (b ^ half) of the row.
+template <bool KC>
+struct WideOp;
+
+template <>
+struct WideOp<true> {
+    static constexpr int reads = 1;  // LDS read instructions per fragment
+    __device__ static int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+    // Byte offset, from the stage's origin in global memory, of LDS vector s.
+    __device__ static uint32_t src(int s, int64_t ld)
+    {
+        const int r = s / (kBK / 4), v = (s % (kBK / 4)) ^ swz(r);
+        return uint32_t((int64_t(r) * ld + 4 * v) * 4);
+    }
+    __device__ static const char *origin(const float *X, int p0, int64_t ld)
+    {
+        return reinterpret_cast<const char *>(X + int64_t(p0) * ld);
+    }
+    __device__ static int64_t stage_bytes(int64_t) { return int64_t(kBK) * 4; }
+    __device__ static int frag(int p, int l32, int half, int g)
+    {
+        const int r = p + l32;
+        return 4 * (r * (kBK / 4) + ((2 * g + half) ^ swz(r)));
+    }
+    __device__ static int block(int b, int) { return b * 32 * kBK; }
+    __device__ static v4f read(const float *t) { return *reinterpret_cast<const v4f *>(t); }
+};
+
+template <>
+struct WideOp<false> {
+    static constexpr int reads = 2;  // two ds_read2 of rows k, k + 1 and k + 2, k + 3
+    __device__ static int swz(int r) { return ((r >> 2) & 1) << 3; }
+    __device__ static uint32_t src(int s, int64_t ld)
+    {
+        const int r = s / (kP / 4), v = (s % (kP / 4)) ^ swz(r);
+        return uint32_t((int64_t(r) * ld + 4 * v) * 4);
+    }
+    __device__ static const char *origin(const float *X, int p0, int64_t)
+    {
+        return reinterpret_cast<const char *>(X + p0);
+    }
+    __device__ static int64_t stage_bytes(int64_t ld) { return int64_t(kBK) * ld * 4; }
+    __device__ static int frag(int p, int l32, int half, int g) { return (8 * g + 4 * half) * kP + p + l32; }
+    __device__ static int block(int b, int half) { return 32 * (b ^ half); }
+    __device__ static v4f read(const float *t) { return v4f{t[0], t[kP], t[2 * kP], t[3 * kP]}; }
+};
 
 // Wait until at most N of this wave's vector-memory operations (the
 // global -> LDS copies) are outstanding.  gfx9 encoding: vmcnt in bits 3:0
@@ -77,6 +129,7 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+template <bool A_KC, bool B_KC>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2))) void
 wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__restrict__ B, int64_t ldb,
             float *__restrict__ C, int64_t ldc, int tiles_m, int tiles_n, int tile_base, int64_t stride_a,
@@ -96,28 +149,22 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
     const int wm = (wave / 2) * 64, wn = (wave % 2) * 128;
     const int half = lane / 32, l32 = lane % 32;
 
+    using OA = WideOp<A_KC>;
+    using OB = WideOp<B_KC>;
     // Byte offsets, from the stage's origin in global memory, of the vector
     // this lane copies in each of its wave's 1 KB pieces.  Piece q of wave w
-    // fills LDS vectors s = (w * pieces + q) * 64 + lane; LDS slot s % rowlen
-    // of row s / rowlen holds the logical vector slot ^ swz(row).
+    // fills LDS vectors s = (w * pieces + q) * 64 + lane.
     uint32_t oa[kAPieces], ob[kBPieces];
 #pragma unroll
-    for (int q = 0; q < kAPieces; ++q) {
-        const int s = (wave * kAPieces + q) * 64 + lane;
-        const int r = s / kAVec, v = (s % kAVec) ^ swz_a(r);
-        oa[q] = uint32_t((int64_t(r) * lda + 4 * v) * 4);
-    }
+    for (int q = 0; q < kAPieces; ++q) oa[q] = OA::src((wave * kAPieces + q) * 64 + lane, lda);
 #pragma unroll
-    for (int q = 0; q < kBPieces; ++q) {
-        const int s = (wave * kBPieces + q) * 64 + lane;
-        const int r = s / kBVec, v = (s % kBVec) ^ swz_b(r);
-        ob[q] = uint32_t((int64_t(r) * ldb + 4 * v) * 4);
-    }
-    const char *ga = reinterpret_cast<const char *>(A + int64_t(m0) * lda);
-    const char *gb = reinterpret_cast<const char *>(B + n0);
+    for (int q = 0; q < kBPieces; ++q) ob[q] = OB::src((wave * kBPieces + q) * 64 + lane, ldb);
+    const char *ga = OA::origin(A, m0, lda);
+    const char *gb = OB::origin(B, n0, ldb);
+    const int64_t a_step = OA::stage_bytes(lda), b_step = OB::stage_bytes(ldb);
     auto copy_stage = [&](float *dst, int st) {
-        const char *sa = ga + int64_t(st) * kBK * 4;
-        const char *sb = gb + int64_t(st) * kBK * ldb * 4;
+        const char *sa = ga + st * a_step;
+        const char *sb = gb + st * b_step;
 #pragma unroll
         for (int q = 0; q < kAPieces; ++q)
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(sa + oa[q]),
@@ -128,22 +175,19 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
                                              dst + kAFloats + (wave * kBPieces + q) * 256, 16, 0, 0);
     };
 
-    // Fragment addresses (floats from a stage's origin) for k group g.
-    // A: row wm + l32 (block i adds 32 rows), logical vector 2 g + half.
-    // B: rows k = 8 g + 4 half + u, column p = wn + 32 j + l32.  Its vector
-    // p / 4 has bits 3-4 equal to j (wn / 4 is 0 or 32, l32 / 4 < 8), and
-    // swz_b(k) = 8 * half, so block j of this lane sits at float
-    // wn + l32 + 32 * (j ^ half) of the row.
-    int a_off[4], b_off[4];
+    // Fragment addresses (floats from a stage's origin) for k group g and
+    // block 0 of this wave (wm and wn are multiples of 64), and the offsets
+    // of its other blocks.
+    int a_off[4], b_off[4], it[kFM], jt[kFN];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const int r = wm + l32;
-        a_off[g] = 4 * (r * kAVec + ((2 * g + half) ^ swz_a(r)));
-        b_off[g] = kAFloats + (8 * g + 4 * half) * kBN + wn + l32;
+        a_off[g] = OA::frag(wm, l32, half, g);
+        b_off[g] = kAFloats + OB::frag(wn, l32, half, g);
     }
-    int jt[kFN];
 #pragma unroll
-    for (int j = 0; j < kFN; ++j) jt[j] = 32 * (j ^ half);
+    for (int i = 0; i < kFM; ++i) it[i] = OA::block(i, half);
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) jt[j] = OB::block(j, half);
 
     v16f acc[kFM][kFN];
 #pragma unroll
@@ -165,12 +209,9 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
         v4f fa[2][kFM], fb[2][kFN];
         auto read = [&](int g, int sl) {
 #pragma unroll
-            for (int i = 0; i < kFM; ++i) fa[sl][i] = *reinterpret_cast<const v4f *>(c + a_off[g] + i * 32 * kBK);
+            for (int i = 0; i < kFM; ++i) fa[sl][i] = OA::read(c + a_off[g] + it[i]);
 #pragma unroll
-            for (int j = 0; j < kFN; ++j) {
-                const float *col = c + b_off[g] + jt[j];
-                fb[sl][j] = v4f{col[0], col[kBN], col[2 * kBN], col[3 * kBN]};
-            }
+            for (int j = 0; j < kFN; ++j) fb[sl][j] = OB::read(c + b_off[g] + jt[j]);
         };
         read(0, 0);
 #pragma unroll
@@ -185,14 +226,17 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
                     for (int j = 0; j < kFN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[sl][i][u], fb[sl][j][u], acc[i][j], 0, 0, 0);
             if (g + 1 < 4) {
-                // the next group's 10 LDS reads (2 of A, 4 x 2 of B), one
-                // per 3 of this group's 32 MFMAs
+                // the next group's LDS reads spread evenly over this
+                // group's 32 MFMAs
+                constexpr int kMfma = 4 * kFM * kFN;
+                constexpr int kReads = kFM * OA::reads + kFN * OB::reads;
+                constexpr int per = kMfma / kReads;
 #pragma unroll
-                for (int q = 0; q < 10; ++q) {
+                for (int q = 0; q < kReads; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if (kMfma > per * kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - per * kReads, 0);
             }
         }
     }
@@ -224,10 +268,12 @@ bool offsets_fit(int rows, int64_t ld) { return (int64_t(rows) * ld + ld) * 4 < 
 bool mfma_wide_fits(const Problem &p)
 {
     const bool batched = p.batch > 1;
-    return !p.transA && !p.transB && p.k_total == 0 && p.M % kBM == 0 && p.N % kBN == 0 && p.K % kBK == 0 &&
-           p.K >= kBK && p.K <= kWideMaxK && vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb) &&
-           (!batched || (p.stride_a % 4 == 0 && p.stride_b % 4 == 0)) && offsets_fit(kBM, p.lda) &&
-           offsets_fit(kBK, p.ldb) && int64_t(p.M / kBM) * (p.N / kBN) <= kMaxGrid;
+    // rows of one stage as stored: 256 when k runs along the rows, else 32
+    const int a_rows = p.transA ? kBK : kBM, b_rows = p.transB ? kBN : kBK;
+    return p.k_total == 0 && p.M % kBM == 0 && p.N % kBN == 0 && p.K % kBK == 0 && p.K >= kBK &&
+           p.K <= kWideMaxK && vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb) &&
+           (!batched || (p.stride_a % 4 == 0 && p.stride_b % 4 == 0)) && offsets_fit(a_rows, p.lda) &&
+           offsets_fit(b_rows, p.ldb) && int64_t(p.M / kBM) * (p.N / kBN) <= kMaxGrid;
 }
 
 bool mfma_wide_preferred(const Problem &p)
@@ -235,15 +281,27 @@ bool mfma_wide_preferred(const Problem &p)
     return mfma_wide_fits(p) && int64_t(p.M / kBM) * (p.N / kBN) * p.batch >= kWideMinTiles;
 }
 
-hipError_t launch_mfma_wide(const Problem &p, hipStream_t s)
+namespace {
+template <bool A_KC, bool B_KC>
+void launch_layout(const Problem &p, hipStream_t s)
 {
     const int tiles_m = p.M / kBM, tiles_n = p.N / kBN;
     for (int64_t b0 = 0; b0 < p.batch; b0 += kMaxGridY) {
         const int64_t nb = p.batch - b0 < kMaxGridY ? p.batch - b0 : kMaxGridY;
-        wide_kernel<<<dim3(unsigned(tiles_m * tiles_n), unsigned(nb)), dim3(kThreads), 0, s>>>(
+        wide_kernel<A_KC, B_KC><<<dim3(unsigned(tiles_m * tiles_n), unsigned(nb)), dim3(kThreads), 0, s>>>(
             p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, 0, p.stride_a, p.stride_b, p.stride_c, b0,
             p.bias, p.act);
     }
+}
+}  // namespace
+
+hipError_t launch_mfma_wide(const Problem &p, hipStream_t s)
+{
+    // A is k-contiguous when untransposed; B when transposed.
+    if (!p.transA)
+        p.transB ? launch_layout<true, true>(p, s) : launch_layout<true, false>(p, s);
+    else
+        p.transB ? launch_layout<false, true>(p, s) : launch_layout<false, false>(p, s);
     return hipGetLastError();
 }
 

@@ -77,10 +77,10 @@ enum gemm_f32_algo {
                                        FP32 sum per output (relative error about
                                        2^-24 * sqrt(K / 12) on zero-mean data, so
                                        K <= 1024 keeps it below 1e-6).  Only for
-                                       transA = transB = 0, M and N multiples of 256,
-                                       K a multiple of 32 and at most 1024, A and B
-                                       16-byte aligned with lda and ldb multiples of
-                                       4; any other non-empty problem returns -13.
+                                       M and N multiples of 256, K a multiple of 32
+                                       and at most 1024, A and B 16-byte aligned with
+                                       lda and ldb multiples of 4 (either transpose);
+                                       any other non-empty problem returns -13.
                                        AUTO takes it for such problems with at least
                                        256 tiles. */
 };

@@ -91,16 +91,16 @@ ALIGNED = 0x10000  # 16-byte aligned, never dereferenced
 
 
 @pytest.mark.parametrize("kwargs", [
-    dict(ta=1), dict(tb=1),                          # transposed operands
     dict(M=300), dict(N=200),                        # not multiples of 256
     dict(K=1056), dict(K=40), dict(K=16),            # K above 1024 or not a multiple of 32
     dict(lda=66), dict(ldb=258),                     # leading dimensions not multiples of 4
+    dict(ta=1, lda=258), dict(tb=1, ldb=66),         # the same with transposed operands
     dict(A=ALIGNED + 4), dict(B=ALIGNED + 8),        # operands not 16-byte aligned
 ], ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
 def test_wide_refuses_problems_outside_its_domain(kwargs):
-    """The 256 x 256 kernel runs only untransposed, aligned products with M
-    and N multiples of 256 and K a multiple of 32 up to 1024: anything else
-    is -13, decided on the host before any HIP call."""
+    """The 256 x 256 kernel runs only aligned products with M and N multiples
+    of 256 and K a multiple of 32 up to 1024 (either transpose): anything
+    else is -13, decided on the host before any HIP call."""
     args = dict(M=256, N=256, K=64, A=ALIGNED, B=ALIGNED, C=ALIGNED)
     args.update(kwargs)
     assert call(fn="gemm_f32_ex", algo=WIDE, **args) == -13

@@ -1,5 +1,5 @@
 """GPU parity of the 256 x 256 MFMA kernel (one running FP32 sum per output,
-for untransposed aligned products with K <= 1024).
+for aligned products with K <= 1024, any transposes).
 
 Marked ``gpu``.  The kernel is called directly (GEMM_F32_ALGO_MFMA_WIDE) on
 problems in its domain, and through the automatic choice, the batched entry
@@ -32,45 +32,54 @@ def device():
 EXACT_SHAPES = [(256, 256, 32), (256, 512, 64), (512, 768, 96), (768, 256, 1024)]
 
 
+LAYOUTS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+
+
 @pytest.mark.parametrize("extra", [0, 4])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_integer_exact(oracle, shape, extra):
-    """Integers in [-8, 8] (every partial sum exact): bit-for-bit equality,
-    which pins the copy swizzle, the fragment map and the store map; padded
-    leading dimensions (multiples of 4) and C's padding untouched."""
+def test_integer_exact(oracle, shape, ta, tb, extra):
+    """Integers in [-8, 8] (every partial sum exact): bit-for-bit equality in
+    every layout, which pins the copy swizzles, the fragment maps and the
+    store map; padded leading dimensions (multiples of 4) and C's padding
+    untouched."""
     M, N, K = shape
-    w = gi.make_case(M, N, K, 0, 0, extra, "int8", seed=M + 5 * N + 11 * K + extra)
+    w = gi.make_case(M, N, K, ta, tb, extra, "int8", seed=M + 5 * N + 11 * K + extra + 2 * ta + tb)
     A, B = w.make_a(), w.make_b()
-    out = P.run_gemm("mfmawide", A, B, w.make_c(), M, N, K, 0, 0, label=w.name)
+    out = P.run_gemm("mfmawide", A, B, w.make_c(), M, N, K, ta, tb, label=w.name)
     P.check_padding(out, N)
-    P.check_exact(out[:, :N], oracle.gemm(A, B, M, N, K), w.name)
+    P.check_exact(out[:, :N], oracle.gemm(A, B, M, N, K, ta, tb), w.name)
 
 
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("dist", ["u11", "n01"])
 @pytest.mark.parametrize("shape", [(512, 512, 1024), (1024, 768, 512)], ids=lambda s: "x".join(map(str, s)))
-def test_float_tolerance(oracle, shape, dist):
+def test_float_tolerance(oracle, shape, dist, ta, tb):
     """Floating-point data within the 1e-6 bounds at K up to 1024."""
     M, N, K = shape
-    w = gi.make_case(M, N, K, 0, 0, 4, dist, seed=M + N + K)
+    w = gi.make_case(M, N, K, ta, tb, 4, dist, seed=M + N + K + 2 * ta + tb)
     A, B = w.make_a(), w.make_b()
-    out = P.run_gemm("mfmawide", A, B, w.make_c(), M, N, K, 0, 0, label=w.name)
+    out = P.run_gemm("mfmawide", A, B, w.make_c(), M, N, K, ta, tb, label=w.name)
     P.check_padding(out, N)
-    frob = P.check_close(out[:, :N], oracle.gemm(A, B, M, N, K), K, w.name)
+    frob = P.check_close(out[:, :N], oracle.gemm(A, B, M, N, K, ta, tb), K, w.name)
     print(f"wide {w.name} relFrob={frob:.3g}")
 
 
-@pytest.mark.parametrize("shape", [(4096, 4096, 1024), (8192, 4096, 1024)], ids=lambda s: "x".join(map(str, s)))
-def test_auto_selects_it_at_full_size(oracle, shape):
+@pytest.mark.parametrize("shape,ta,tb", [((4096, 4096, 1024), 0, 0), ((8192, 4096, 1024), 0, 0),
+                                         ((8192, 4096, 1024), 0, 1), ((4096, 4096, 512), 1, 0),
+                                         ((4096, 4096, 256), 1, 1)],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_auto_selects_it_at_full_size(oracle, shape, ta, tb):
     """256 and 512 tiles: the automatic choice runs this kernel (bit-for-bit
     equal to the direct call), and sampled entries meet the bounds."""
     M, N, K = shape
-    w = gi.make_case(M, N, K, 0, 0, 0, "n01", seed=3 * M + K)
+    w = gi.make_case(M, N, K, ta, tb, 0, "n01", seed=3 * M + K + ta + 2 * tb)
     A, B = w.make_a(), w.make_b()
-    auto = P.run_gemm("auto", A, B, w.make_c(), M, N, K, 0, 0, label=w.name)
-    wide = P.run_gemm("mfmawide", A, B, w.make_c(), M, N, K, 0, 0, label=w.name)
+    auto = P.run_gemm("auto", A, B, w.make_c(), M, N, K, ta, tb, label=w.name)
+    wide = P.run_gemm("mfmawide", A, B, w.make_c(), M, N, K, ta, tb, label=w.name)
     assert np.array_equal(auto, wide)
     rows, cols = gi.sample_entries(M, N, 3000, seed=23)
-    ref = oracle.entries(A, B, M, N, K, 0, 0, rows, cols)
+    ref = oracle.entries(A, B, M, N, K, ta, tb, rows, cols)
     frob = P.check_close(wide[rows, cols], ref, K, f"{w.name} sampled")
     print(f"wide {w.name} sampled relFrob={frob:.3g}")
 
@@ -79,10 +88,11 @@ def _batched(w, A, B):
     import torch
     import dense_fp32_matrix_gemm_amd as g
     dA, dB, dC = P.to_device(A), P.to_device(B), P.to_device(w.make_c())
-    P.note(f"wide batched {w.name} batch={w.batch}")
+    P.note(f"wide batched {w.name} batch={w.batch} t{w.transA}{w.transB}")
     st = g.gemm_f32_strided_batched(w.M, w.N, w.K, dA.data_ptr(), w.lda_, w.stride_a,
                                     dB.data_ptr(), w.ldb_, w.stride_b, dC.data_ptr(), w.ldc_,
-                                    w.stride_c, w.batch, 0, 0, torch.cuda.current_stream().cuda_stream)
+                                    w.stride_c, w.batch, w.transA, w.transB,
+                                    torch.cuda.current_stream().cuda_stream)
     assert st == 0, g.gemm_f32_strerror(st)
     torch.cuda.synchronize()
     flat = dC.cpu().numpy().reshape(w.batch, w.stride_c)
@@ -90,27 +100,31 @@ def _batched(w, A, B):
     return body[:, :, :w.N], flat
 
 
+@pytest.mark.parametrize("tb", [0, 1])
 @pytest.mark.parametrize("dist", ["int8", "n01"])
-def test_batched(dist):
-    """64 products of 512 x 512 x 64 (256 tiles): the batched entry point
-    selects this kernel; exact on integers, and on floats each product is
-    bit-for-bit the direct single-product call and within the bounds."""
-    w = gi.Workload("wide-batch", 512, 512, 64, 91, 92, dist, dist, batch=64, ldc=512 + 4, gap=8)
+def test_batched(dist, tb):
+    """64 products of 512 x 512 x 64 (256 tiles; with B transposed this is
+    the attention-score batch): the batched entry point selects this kernel;
+    exact on integers, and on floats each product is bit-for-bit the direct
+    single-product call and within the bounds."""
+    w = gi.Workload("wide-batch", 512, 512, 64, 91 + tb, 92, dist, dist, transB=tb, batch=64,
+                    ldc=512 + 4, gap=8)
     A, B = w.make_a(), w.make_b()
     got, flat = _batched(w, A, B)
     pad = np.concatenate([flat[:, :w.M * w.ldc_].reshape(w.batch, w.M, w.ldc_)[:, :, w.N:].reshape(-1),
                           flat[:, w.M * w.ldc_:].reshape(-1)])
     assert np.all(pad == np.float32(gi.OUTPUT_PAD))
-    ref = oracle_pkg.gemm_ref_batched(A, B, w.M, w.N, w.K, 0, 0, w.lda_, w.stride_a, w.ldb_,
+    ref = oracle_pkg.gemm_ref_batched(A, B, w.M, w.N, w.K, 0, tb, w.lda_, w.stride_a, w.ldb_,
                                       w.stride_b, w.batch)
+    b_rows = w.N if tb else w.K
     for b in (0, 1, 37, 63):
         if dist == "int8":
             P.check_exact(got[b], ref[b], f"batch[{b}]")
             continue
         P.check_close(got[b], ref[b], w.K, f"batch[{b}]")
         Ab = A.reshape(-1)[b * w.stride_a: b * w.stride_a + w.M * w.lda_].reshape(w.M, w.lda_)
-        Bb = B.reshape(-1)[b * w.stride_b: b * w.stride_b + w.K * w.ldb_].reshape(w.K, w.ldb_)
-        one = P.run_gemm("mfmawide", Ab, Bb, gi.output_matrix(w.M, w.N), w.M, w.N, w.K, 0, 0,
+        Bb = B.reshape(-1)[b * w.stride_b: b * w.stride_b + b_rows * w.ldb_].reshape(b_rows, w.ldb_)
+        one = P.run_gemm("mfmawide", Ab, Bb, gi.output_matrix(w.M, w.N), w.M, w.N, w.K, 0, tb,
                          label=f"batch[{b}] alone")
         assert np.array_equal(one, got[b])
 
