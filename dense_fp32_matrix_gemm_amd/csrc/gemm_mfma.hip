@@ -685,6 +685,12 @@ constexpr int kShortK = 1024;
 // workgroup, so short products stay on the 128 x 128 tile (the 64-product
 // attention-score batch, K = 64: 59.7 vs 55.9 TFLOP/s).
 constexpr int kHugeMinK = 512;
+// Long products whose large tiles fill whole rounds of one per CU leave no
+// tail, and the 256 x 128 tile's lower copy traffic wins below
+// GEMM_MFMA_HUGE_FROM too (the 8192 x 1024 x 4096 input-gradient product,
+// 256 tiles: 138.7 vs 135.7 TFLOP/s).
+constexpr int kHugeLongK = 2048;
+constexpr int kCUs = 256;  // MI355X
 
 }  // namespace
 
@@ -701,7 +707,8 @@ hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
         const int64_t huge_tiles =
             int64_t(ceil_div(p.M, Huge::BM)) * ceil_div(p.N, Huge::BN) * p.batch;
         const bool huge_fits = 4 * area >= 3 * huge_tiles * Huge::BM * Huge::BN;
-        const bool huge = huge_tiles >= GEMM_MFMA_HUGE_FROM && huge_fits && p.K >= kHugeMinK;
+        const bool whole_rounds = p.K >= kHugeLongK && huge_tiles % kCUs == 0;
+        const bool huge = (huge_tiles >= GEMM_MFMA_HUGE_FROM || whole_rounds) && huge_fits && p.K >= kHugeMinK;
         tile = small ? Small::BM : huge ? Huge::BM : Default::BM;
     }
     if (tile == Small::BM) {
