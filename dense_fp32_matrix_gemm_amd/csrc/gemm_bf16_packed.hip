@@ -63,16 +63,6 @@ __device__ __forceinline__ void unroll_for(F &&f)
     }
 }
 
-// Wait until at most N of this wave's vector-memory operations are
-// outstanding (they complete in issue order).  gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima.
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 // BM x BN of C per workgroup, BK bf16 per stage, WAVES_M x WAVES_N waves,
 // NBUF LDS stage buffers (copies in flight: NBUF - 1), GROUP_M tile-rows per
 // group of the launch order, FOLD stages per accumulation chunk (0: one

@@ -250,17 +250,6 @@ struct Tile {
     }
 };
 
-// Wait until at most N of this wave's vector-memory operations (here: the
-// global->LDS copies) are outstanding; they complete in issue order.
-// gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8
-// left at their maxima (no wait).
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 template <class Cfg, bool A_KC, bool B_KC, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::threads, Cfg::threads),
                           amdgpu_waves_per_eu(Cfg::wpe, Cfg::wpe))) void
@@ -690,7 +679,6 @@ constexpr int kHugeMinK = 512;
 // GEMM_MFMA_HUGE_FROM too (the 8192 x 1024 x 4096 input-gradient product,
 // 256 tiles: 138.7 vs 135.7 TFLOP/s).
 constexpr int kHugeLongK = 2048;
-constexpr int kCUs = 256;  // MI355X
 
 }  // namespace
 

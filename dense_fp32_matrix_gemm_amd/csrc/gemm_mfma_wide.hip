@@ -52,7 +52,7 @@ constexpr int kAPieces = kAFloats / 256 / kWaves;  // 1 KB copies per wave per s
 constexpr int kBPieces = kBFloats / 256 / kWaves;
 constexpr int kGroupM = 4;  // tile-rows per group of the launch order
 constexpr int kWideMaxK = 1024;
-constexpr int kWideMinTiles = 256;  // auto selection: at least one tile per CU
+constexpr int kWideMinTiles = kCUs;  // auto selection: at least one tile per CU
 static_assert(kAPieces * kWaves * 256 == kAFloats && kBPieces * kWaves * 256 == kBFloats,
               "each stage splits into whole 1 KB copies per wave");
 
@@ -118,16 +118,6 @@ struct WideOp<false> {
     __device__ static int block(int b, int half) { return 32 * (b ^ half); }
     __device__ static v4f read(const float *t) { return v4f{t[0], t[kP], t[2 * kP], t[3 * kP]}; }
 };
-
-// Wait until at most N of this wave's vector-memory operations (the
-// global -> LDS copies) are outstanding.  gfx9 encoding: vmcnt in bits 3:0
-// and 15:14; expcnt and lgkmcnt left at their maxima.
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 template <bool A_KC, bool B_KC>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2))) void

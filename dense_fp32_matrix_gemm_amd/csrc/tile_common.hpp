@@ -76,7 +76,19 @@ struct Slice {
     }
 };
 
-constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kCUs = 256;  // MI355X: compute units (32 per XCD)
+
+// Wait until at most N of this wave's vector-memory operations (here: the
+// global -> LDS copies) are outstanding; they complete in issue order.
+// gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8
+// left at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Workgroup index -> (tile row, tile column) of a tiles_m x tiles_n grid.
 // Step 1 inverts the round-robin dealing of consecutive workgroups to the
