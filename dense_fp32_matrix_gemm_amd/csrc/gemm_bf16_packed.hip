@@ -401,9 +401,20 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
 #ifndef GEMM_PACKED_SMALL_CONFIG
 #define GEMM_PACKED_SMALL_CONFIG 128, 128, 32, 4, 2, 4, 8, 4
 #endif
+// SmallDeep: the small tile with 64-k stages in a four-buffer ring, runs of
+// 256 k and staggered copies, for problems whose tiles are all interior and
+// whose stages are all whole (1024 x 4096 x 8192: 835-844 vs 695-702
+// TFLOP/s; 1024^3: 176-186 vs 158).  The ragged 2049 x 3071 x 769 product
+// stays on 32-k stages (349 vs 292-295): its partial last stage and its
+// register-staged edge tiles cost more with deeper stages.
+#ifndef GEMM_PACKED_SMALL_DEEP_CONFIG
+#define GEMM_PACKED_SMALL_DEEP_CONFIG 128, 128, 64, 4, 2, 4, 8, 4, 1
+#endif
 using Large = Config<GEMM_PACKED_LARGE_CONFIG>;
 using Mid = Config<GEMM_PACKED_MID_CONFIG>;
 using Small = Config<GEMM_PACKED_SMALL_CONFIG>;
+using SmallDeep = Config<GEMM_PACKED_SMALL_DEEP_CONFIG>;
+static_assert(SmallDeep::BM == Small::BM && SmallDeep::BN == Small::BN, "one small tile, two stage depths");
 
 // The large tile from one tile per CU: below that (e.g. 8192 x 1024, 128
 // large tiles) half the CUs would idle, and 128 x 128 tiles are faster
@@ -561,6 +572,8 @@ hipError_t launch_bf16_packed(const PackedProblem &p, hipStream_t s, int tile)
         dispatch<Large>(p, s);
     else if (tile == Mid::BM * Mid::BN && p.K <= kLargeMaxK)
         dispatch<Mid>(p, s);
+    else if (p.M % SmallDeep::BM == 0 && p.N % SmallDeep::BN == 0 && p.K % SmallDeep::BK == 0)
+        dispatch<SmallDeep>(p, s);
     else
         dispatch<Small>(p, s);
     return hipGetLastError();
