@@ -574,6 +574,9 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #ifndef GEMM_MFMA_KK_CONFIG
 #define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1, 1
 #endif
+#ifndef GEMM_MFMA_ONE_ROUND_CONFIG
+#define GEMM_MFMA_ONE_ROUND_CONFIG 128, 128, 32, 4, 2, 4, 8, 1, 1, 1, 3, 6, 1, 1, 1
+#endif
 #ifndef GEMM_MFMA_NARROW_CONFIG
 #define GEMM_MFMA_NARROW_CONFIG 128, 64, 64, 4, 2, 4, 8, 7, 1, 1, 2, 4, 1, 1
 #endif
@@ -601,6 +604,13 @@ using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // 8192 x 1024 x 4096 input-gradient product: 125 -> 129 TFLOP/s; with
 // raised MFMA issue priority 131.1 -> 135.1).
 using DefaultKK = Config<GEMM_MFMA_KK_CONFIG>;
+// 128 x 128 tile for grids of at most one tile per CU, where no second
+// workgroup shares a CU: three stage buffers (96 KB), 192-k accumulation
+// chunks, raised MFMA issue priority and staggered copies, as on the
+// 256 x 128 tile (the 1024 x 4096 x 8192 weight gradient, 256 tiles:
+// 137.4-137.6 vs 132.7-133.1 TFLOP/s; the priority or the stagger alone
+// 133.2 / 134.6).
+using OneRound = Config<GEMM_MFMA_ONE_ROUND_CONFIG>;
 // 128 x 64 tile for outputs at most 64 columns wide (8 waves of 32 x 32,
 // 64-k stages in two buffers, 256-k accumulation chunks): a quarter fewer
 // bytes copied per flop than the 64 x 64 tile, and one tile per CU from
@@ -721,10 +731,16 @@ hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
         else
             dispatch_layout<Small>(p, s);
     }
-    else if (tile == Huge::BM)
+    else if (tile == Huge::BM) {
         dispatch_layout<Huge>(p, s);
-    else
-        dispatch_layout<Default, DefaultKK>(p, s);
+    }
+    else {
+        const int64_t tiles = int64_t(ceil_div(p.M, Default::BM)) * ceil_div(p.N, Default::BN) * p.batch;
+        if (tiles <= kCUs)
+            dispatch_layout<OneRound, DefaultKK>(p, s);
+        else
+            dispatch_layout<Default, DefaultKK>(p, s);
+    }
     return hipGetLastError();
 }
 
