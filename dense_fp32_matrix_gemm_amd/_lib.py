@@ -19,6 +19,10 @@ ALGO_MFMA_TILE128, ALGO_MFMA_TILE64, ALGO_MFMA_TILE256, ALGO_MFMA_WIDE = 5, 6, 7
 ALGOS = {"auto": ALGO_AUTO, "mfma": ALGO_MFMA, "fma": ALGO_FMA, "tiled": ALGO_TILED,
          "naive": ALGO_NAIVE, "mfma128": ALGO_MFMA_TILE128, "mfma64": ALGO_MFMA_TILE64,
          "mfma256": ALGO_MFMA_TILE256, "mfmawide": ALGO_MFMA_WIDE}
+# gemm_f32_plan codes (enum gemm_f32_plan_code)
+PLANS = {0: "nothing", 1: "zero-fill", 2: "mfma-256x256", 3: "mfma-256x128", 4: "mfma-128x128",
+         5: "mfma-128x128-one-round", 6: "mfma-128x128-kk", 7: "mfma-128x64", 8: "mfma-64x64",
+         9: "mfma-64x64-ring"}
 
 # Every symbol include/gemm_f32.h declares, with (restype, argtypes).
 _i64, _ptr, _int, _flt = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
@@ -43,6 +47,7 @@ SIGNATURES = {
     "rows_normalize_f32": (_int, [_i64, _i64, _flt, _ptr, _i64, _ptr, _i64, _ptr]),
     "rows_normalize_backward_f32": (_int, [_i64, _i64, _flt, _ptr, _i64, _ptr, _i64, _ptr, _i64,
                                            _ptr]),
+    "gemm_f32_plan": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _int, _i64, _i64, _i64]),
     "gemm_f32_version": (_int, []),
 }
 
@@ -160,3 +165,7 @@ def gemm_f32_strerror(status: int) -> str:
 
 def gemm_f32_version() -> int:
     return _call("gemm_f32_version")
+
+
+def gemm_f32_plan(M, N, K, A, lda, B, ldb, ldc, transA, transB, strideA=0, strideB=0, batch=1) -> int:
+    return _call("gemm_f32_plan", M, N, K, A, lda, B, ldb, ldc, transA, transB, strideA, strideB, batch)

@@ -304,6 +304,26 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda
     return err == hipSuccess ? 0 : int(err);
 }
 
-int gemm_f32_version(void) { return 10600; }
+int gemm_f32_plan(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                  int64_t ldb, int64_t ldc, int transA, int transB, int64_t strideA,
+                  int64_t strideB, int64_t batch)
+{
+    // gemm_f32's checks without the pointer checks; its ldc and transpose
+    // positions (-9, -10, -11) are one place earlier in this prototype.
+    const int bad = validate(M, N, K, A, lda, B, ldb, nullptr, ldc, transA, transB, false);
+    if (bad) return bad <= -9 ? bad + 1 : bad;
+    if (strideA < 0) return -11;
+    if (strideB < 0) return -12;
+    if (batch < 1 || batch > kDimLimit) return -13;
+    if (M == 0 || N == 0) return GEMM_F32_PLAN_NOTHING;
+    if (K == 0) return GEMM_F32_PLAN_ZERO_FILL;
+    Problem p{int(M), int(N), int(K), A, lda, B, ldb, nullptr, ldc, transA, transB};
+    p.stride_a = batch > 1 ? strideA : 0;
+    p.stride_b = batch > 1 ? strideB : 0;
+    p.batch = batch;
+    return gemmf32::plan_mfma(p, 0);
+}
+
+int gemm_f32_version(void) { return 10700; }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "gemm_f32.h"
+
 #include <cstdint>
 
 namespace gemmf32 {
@@ -41,6 +43,9 @@ hipError_t launch_fma(const Problem &p, hipStream_t stream);
 // tile: 0 chooses by problem size (the 256 x 256 kernel when it is preferred);
 // 256 (256 x 128), 128 or 64 forces that tile.
 hipError_t launch_mfma(const Problem &p, hipStream_t stream, int tile);
+// The configuration launch_mfma runs for p and tile: a gemm_f32_plan_code
+// (one of the GEMM_F32_PLAN_MFMA_* values).  Host only; launches nothing.
+int plan_mfma(const Problem &p, int tile);
 // The 256 x 256 MFMA kernel with one running sum per output
 // (gemm_mfma_wide.hip).  fits: the problem is in its domain (any
 // transposes, M and N multiples of 256, K a multiple of 32 and at most

@@ -701,9 +701,9 @@ constexpr int kHugeLongK = 2048;
 
 }  // namespace
 
-hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
+int plan_mfma(const Problem &p, int tile)
 {
-    if (tile == 0 && mfma_wide_preferred(p)) return launch_mfma_wide(p, s);
+    if (tile == 0 && mfma_wide_preferred(p)) return GEMM_F32_PLAN_MFMA_256X256;
     bool narrow = false;
     if (tile == 0) {
         const int64_t big_tiles =
@@ -721,25 +721,28 @@ hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
         const int64_t narrow_tiles = int64_t(ceil_div(p.M, Narrow::BM)) * p.batch;
         narrow = small && p.N <= Narrow::BN && narrow_tiles >= kCUs;
     }
-    if (narrow) {
-        dispatch_layout<Narrow>(p, s);
-    }
-    else if (tile == Small::BM) {
+    if (narrow) return GEMM_F32_PLAN_MFMA_128X64;
+    if (tile == Small::BM) {
         const int64_t small_tiles = int64_t(ceil_div(p.M, Small::BM)) * ceil_div(p.N, Small::BN) * p.batch;
-        if (small_tiles >= GEMM_MFMA_SMALL_DEEP_FROM)
-            dispatch_layout<SmallDeep>(p, s);
-        else
-            dispatch_layout<Small>(p, s);
+        return small_tiles >= GEMM_MFMA_SMALL_DEEP_FROM ? GEMM_F32_PLAN_MFMA_64X64_RING : GEMM_F32_PLAN_MFMA_64X64;
     }
-    else if (tile == Huge::BM) {
-        dispatch_layout<Huge>(p, s);
-    }
-    else {
-        const int64_t tiles = int64_t(ceil_div(p.M, Default::BM)) * ceil_div(p.N, Default::BN) * p.batch;
-        if (tiles <= kCUs)
-            dispatch_layout<OneRound, DefaultKK>(p, s);
-        else
-            dispatch_layout<Default, DefaultKK>(p, s);
+    if (tile == Huge::BM) return GEMM_F32_PLAN_MFMA_256X128;
+    // A is k-contiguous when untransposed; B when transposed.
+    if (!p.transA && p.transB) return GEMM_F32_PLAN_MFMA_128X128_KK;
+    const int64_t tiles = int64_t(ceil_div(p.M, Default::BM)) * ceil_div(p.N, Default::BN) * p.batch;
+    return tiles <= kCUs ? GEMM_F32_PLAN_MFMA_128X128_ONE_ROUND : GEMM_F32_PLAN_MFMA_128X128;
+}
+
+hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
+{
+    switch (plan_mfma(p, tile)) {
+    case GEMM_F32_PLAN_MFMA_256X256: return launch_mfma_wide(p, s);
+    case GEMM_F32_PLAN_MFMA_128X64: dispatch_layout<Narrow>(p, s); break;
+    case GEMM_F32_PLAN_MFMA_64X64_RING: dispatch_layout<SmallDeep>(p, s); break;
+    case GEMM_F32_PLAN_MFMA_64X64: dispatch_layout<Small>(p, s); break;
+    case GEMM_F32_PLAN_MFMA_256X128: dispatch_layout<Huge>(p, s); break;
+    case GEMM_F32_PLAN_MFMA_128X128_ONE_ROUND: dispatch_layout<OneRound, DefaultKK>(p, s); break;
+    default: dispatch_layout<Default, DefaultKK>(p, s); break;
     }
     return hipGetLastError();
 }

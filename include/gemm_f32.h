@@ -85,6 +85,21 @@ enum gemm_f32_algo {
                                        256 tiles. */
 };
 
+/* Kernel configurations of the automatic choice, as reported by
+ * gemm_f32_plan. */
+enum gemm_f32_plan_code {
+    GEMM_F32_PLAN_NOTHING = 0,   /* M or N is 0: nothing is written */
+    GEMM_F32_PLAN_ZERO_FILL = 1, /* K is 0: C is set to 0 */
+    GEMM_F32_PLAN_MFMA_256X256 = 2, /* 256 x 256 tile, one running sum per output */
+    GEMM_F32_PLAN_MFMA_256X128 = 3, /* 256 x 128 tile */
+    GEMM_F32_PLAN_MFMA_128X128 = 4, /* 128 x 128 tile, two workgroups per CU */
+    GEMM_F32_PLAN_MFMA_128X128_ONE_ROUND = 5, /* 128 x 128, at most one tile per CU */
+    GEMM_F32_PLAN_MFMA_128X128_KK = 6, /* 128 x 128, both operands k-contiguous */
+    GEMM_F32_PLAN_MFMA_128X64 = 7,  /* outputs at most 64 columns wide */
+    GEMM_F32_PLAN_MFMA_64X64 = 8,   /* small grids: two k-slices of waves */
+    GEMM_F32_PLAN_MFMA_64X64_RING = 9 /* 64 x 64, 32-k stages in a four-buffer ring */
+};
+
 /* C = op(A) . op(B) on the fastest path (GEMM_F32_ALGO_AUTO). */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *A, int64_t lda,
@@ -247,6 +262,21 @@ int64_t gemm_f32_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int64_t 
  * Messages for -1 .. -11 name gemm_f32's arguments; -12 .. -14 list what the
  * position means for each entry point that uses it. */
 const char *gemm_f32_strerror(int status);
+
+/* The kernel configuration that gemm_f32 would run for these arguments
+ * (and gemm_f32_strided_batched, or gemm_f32_bias_act, for the same
+ * shapes), decided on the host exactly as a call decides it: a
+ * gemm_f32_plan_code.  Nothing is launched and the pointers are never
+ * dereferenced, but their alignment counts (the 256 x 256 tile needs
+ * 16-byte aligned operands and strides).  batch = 1 for a single product.
+ * Returns -i for an invalid argument, numbered in this prototype's order:
+ * -1/-2/-3 a dimension, -5/-7/-8 a leading dimension, -9/-10 a transpose
+ * flag, -11/-12 a negative stride, -13 batch < 1 or >= 2^31. */
+int gemm_f32_plan(int64_t M, int64_t N, int64_t K,
+                  const float *A, int64_t lda,
+                  const float *B, int64_t ldb, int64_t ldc,
+                  int transA, int transB,
+                  int64_t strideA, int64_t strideB, int64_t batch);
 
 /* Library interface version: major * 10000 + minor * 100 + patch. */
 int gemm_f32_version(void);

@@ -10,6 +10,8 @@ import re
 
 import pytest
 
+import gemm_inputs as gi
+
 import dense_fp32_matrix_gemm_amd as g
 from dense_fp32_matrix_gemm_amd import _lib
 
@@ -50,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert g.gemm_f32_version() == 10600
+    assert g.gemm_f32_version() == 10700
 
 
 def call(M=4, N=4, K=4, A=FAKE, lda=None, B=FAKE, ldb=None, C=FAKE, ldc=None,
@@ -160,7 +162,7 @@ def test_operand_layout_from_strides():
 def test_header_is_plain_c():
     """The public header compiles as C with no HIP headers on the include path."""
     import subprocess
-    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10600 ? 0 : 1;}\n"
+    src = "#include \"gemm_f32.h\"\nint main(void){return gemm_f32_version() == 10700 ? 0 : 1;}\n"
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), "-x", "c", "-"],
                        input=src, capture_output=True, text=True)
@@ -354,3 +356,71 @@ def test_bf16_packed_invalid_arguments(kwargs, code):
 def test_bf16_packed_quick_return_without_launch():
     assert packed(M=0, A=None, C=None) == 0
     assert packed(N=0, B=None, C=None) == 0
+
+
+# ---------------------------------------------------------------- plans ---
+
+def plan(M, N, K, ta=0, tb=0, A=ALIGNED, B=ALIGNED, lda=None, ldb=None, ldc=None, sA=0, sB=0, batch=1):
+    lda = max(1, M if ta else K) if lda is None else lda
+    ldb = max(1, K if tb else N) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    code = g.gemm_f32_plan(M, N, K, A, lda, B, ldb, ldc, ta, tb, sA, sB, batch)
+    return g.PLANS.get(code, code)
+
+
+WORKLOAD_PLANS = {
+    "S64": "mfma-64x64", "S1k": "mfma-64x64", "R": "mfma-64x64-ring", "S4k": "mfma-256x128",
+    "T-fwd": "mfma-256x256", "T-dX": "mfma-256x128", "T-dW": "mfma-128x128-one-round",
+    "attn-qk": "mfma-256x256", "attn-pv": "mfma-128x64",
+}
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOAD_PLANS))
+def test_plan_of_each_workload(name):
+    """The automatic choice for every benchmark workload, decided on the
+    host (operands 16-byte aligned, as device allocations are)."""
+    w = gi.WORKLOADS[name]
+    got = plan(w.M, w.N, w.K, w.transA, w.transB, lda=w.lda_, ldb=w.ldb_, ldc=w.ldc_,
+               sA=w.stride_a, sB=w.stride_b, batch=w.batch)
+    assert got == WORKLOAD_PLANS[name]
+
+
+def test_plan_rules_at_their_edges():
+    # 256 x 256 tile: K <= 1024, aligned operands and leading dimensions, >= 256 tiles
+    assert plan(8192, 4096, 1024) == "mfma-256x256"
+    assert plan(8192, 4096, 1024, tb=1) == "mfma-256x256"
+    assert plan(8192, 4096, 1056) == "mfma-256x128"           # K above 1024
+    assert plan(8192, 4096, 1024, A=ALIGNED + 4) == "mfma-256x128"  # A not 16-byte aligned
+    assert plan(8192, 4096, 1024, lda=1026) == "mfma-256x128"       # lda not a multiple of 4
+    assert plan(4096, 2048, 1024) == "mfma-128x128"           # 128 wide tiles: too few
+    # batched: the strides must keep every product aligned
+    assert plan(512, 512, 64, tb=1, sA=512 * 64, sB=512 * 64, batch=64) == "mfma-256x256"
+    assert plan(512, 512, 64, tb=1, sA=512 * 64 + 1, sB=512 * 64, batch=64) == "mfma-128x128-kk"
+    # 256 x 128: 384 tiles, or whole rounds of 256 when K >= 2048
+    assert plan(8192, 1024, 4096, tb=1) == "mfma-256x128"
+    assert plan(8192, 1024, 1024, tb=1, A=ALIGNED + 4) == "mfma-128x128-kk"
+    # 128 x 128: one round or more, and the k-contiguous layout
+    assert plan(1024, 4096, 8192, ta=1) == "mfma-128x128-one-round"
+    assert plan(2048, 4096, 8192, ta=1) == "mfma-256x128"    # 256 large tiles: a whole round
+    assert plan(1536, 4096, 8192, ta=1) == "mfma-128x128"    # 384 tiles, 192 large ones
+    assert plan(2048, 2048, 2048, tb=1) == "mfma-128x128-kk"
+    # narrow outputs: N <= 64 and at least 256 tiles of 128 rows
+    assert plan(512, 64, 512, sA=512 * 512, sB=512 * 64, batch=64) == "mfma-128x64"
+    assert plan(512, 65, 512, sA=512 * 512, sB=512 * 65, batch=64) == "mfma-64x64-ring"  # 1024 small tiles
+    assert plan(512, 64, 512, sA=512 * 512, sB=512 * 64, batch=63) == "mfma-64x64"
+    # degenerate shapes
+    assert plan(0, 64, 64) == "nothing" and plan(64, 0, 64) == "nothing"
+    assert plan(64, 64, 0) == "zero-fill"
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(M=-1), -1), (dict(N=-1), -2), (dict(K=-1), -3), (dict(lda=3), -5), (dict(ldb=3), -7),
+    (dict(ldc=3), -8), (dict(ta=2), -9), (dict(tb=-1), -10), (dict(sA=-1), -11), (dict(sB=-1), -12),
+    (dict(batch=0), -13),
+])
+def test_plan_invalid_arguments(kwargs, code):
+    args = dict(M=4, N=4, K=4)
+    args.update(kwargs)
+    assert g.gemm_f32_plan(args["M"], args["N"], args["K"], ALIGNED, args.get("lda", 4), ALIGNED,
+                           args.get("ldb", 4), args.get("ldc", 4), args.get("ta", 0), args.get("tb", 0),
+                           args.get("sA", 0), args.get("sB", 0), args.get("batch", 1)) == code
