@@ -4,9 +4,10 @@
 
 One step is one C = A.B of the workload (default: the 4096^3 square
 product the throughput metric is quoted on), with A, B and C resident in
-HBM before timing starts.  W untimed steps (by default at least 300 and at
-least 0.3 s of them, so that short kernels are timed at a settled clock;
-the line reports the count), then exactly K steps between
+HBM before timing starts.  At least W untimed steps (300 if W is not
+given), and in either case at least 0.3 s of them, so that the timed steps
+run at a settled clock (the line reports W and the calls actually made),
+then exactly K steps between
 two device synchronisations, timed with HIP events recorded on the stream
 the library launches on (PyTorch's current stream).  Prints ONE JSON line.
 
@@ -190,23 +191,20 @@ def _timed_windows(fn, steps: int, windows: int = 3):
 
 
 def _warm_up(fn, warmup, min_launches: int = 300, min_seconds: float = 0.3):
-    """Run the untimed warm-up: exactly ``warmup`` calls if given; otherwise
-    at least ``min_launches`` calls and at least ``min_seconds`` of them
-    (short kernels need more than 300 launches before the clock has ramped
-    up).  Returns the count."""
+    """Run the untimed warm-up: at least ``warmup`` calls (``min_launches``
+    when not given) and, either way, at least ``min_seconds`` of them.  The
+    clock ramps up over the first tenths of a second of load, so a fixed
+    handful of launches (a few ms of a 1 ms kernel) would time the ramp, not
+    the kernel.  Returns (calls made, seconds spent)."""
     import torch
-    if warmup is not None:
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        return warmup
+    want = min_launches if warmup is None else warmup
     done, t0 = 0, time.perf_counter()
-    while done < min_launches or time.perf_counter() - t0 < min_seconds:
+    while done < want or time.perf_counter() - t0 < min_seconds:
         for _ in range(10):
             fn()
         done += 10
         torch.cuda.synchronize()
-    return done
+    return done, time.perf_counter() - t0
 
 
 def _timed_warm(fn, steps: int):
@@ -429,7 +427,8 @@ def rows_main(args) -> int:
           "normalize-bwd": "normalize_backward"}[args.rows]
     nbytes = row_bytes(op, rows, width)
     torch.cuda.synchronize()
-    args.warmup = _warm_up(step, args.warmup)
+    warm_calls, warm_s = _warm_up(step, args.warmup)
+    args.warmup = args.warmup if args.warmup is not None else warm_calls
     ms, windows = _timed_windows(step, args.steps)
     value = nbytes / (ms * 1e-3) / 1e9
 
@@ -440,6 +439,7 @@ def rows_main(args) -> int:
     line = {
         "metric": f"row reduction HBM throughput ({op}, algorithmic bytes / s)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_calls_made": warm_calls, "warmup_seconds": warm_s,
         "ms_per_step": ms, "windows_ms_per_step": windows, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.rows, "rows": rows, "width": width,
@@ -463,7 +463,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed launches before timing (default: at least 300 and at least 0.3 s)")
+                    help="untimed launches before timing, at least this many and at least 0.3 s of them (default 300)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--algo", default="auto",
                     choices=["auto", "mfma", "mfma256", "mfma128", "mfma64", "mfmawide", "fma", "tiled", "naive", "bf16",
@@ -575,7 +575,8 @@ def main(argv=None) -> int:
 
     flops = w.flops
     torch.cuda.synchronize()
-    args.warmup = _warm_up(step, args.warmup)
+    warm_calls, warm_s = _warm_up(step, args.warmup)
+    args.warmup = args.warmup if args.warmup is not None else warm_calls
     ms, windows = _timed_windows(step, args.steps)
     value = flops / (ms * 1e-3) / 1e12
 
@@ -721,6 +722,8 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls_made": warm_calls,
+        "warmup_seconds": warm_s,
         "ms_per_step": ms,
         "windows_ms_per_step": windows,
         "windows_summary": _window_summary(windows, flops),

@@ -211,10 +211,13 @@ __global__ __launch_bounds__(kThreads) void softmax_long_kernel(Rows sh, int que
         float m = -INFINITY, s = 0.0f;
         for (int c = lane; c < keep; c += kWave) {
             const float z = scale * row[c];
+            // A score of -inf adds exp(-inf) = 0 to the sum; it is skipped
+            // rather than evaluated, since before the lane's first finite
+            // score m is -inf too and exp(-inf - -inf) would be NaN.
             if (z > m) {
                 s = s * expf(m - z) + 1.0f;
                 m = z;
-            } else {
+            } else if (z > -INFINITY) {
                 s += expf(z - m);
             }
         }

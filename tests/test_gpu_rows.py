@@ -131,6 +131,24 @@ def test_softmax_unaligned_and_in_place():
     check_softmax(out.cpu().numpy(), ref, width)
 
 
+def test_softmax_minus_infinity_scores():
+    """Scores of -inf (an additive padding mask) before a lane's first finite
+    score: the streamed path for rows longer than 4096 and the register path
+    at 4096 both give the oracle's values, 0 at every -inf."""
+    rows = 6
+    for width, causal in ((4096, 0), (4097, 0), (5000, 0), (4100, 1)):
+        x = stored(71, rows, width, width + 1)
+        x[:, :130] = -np.inf                # every lane's first two scores
+        x[::2, 300:900:7] = -np.inf         # scattered further on
+        x[3, 4000:] = -np.inf
+        queries = rows                      # causal: rows keep 4095..4100 columns
+        ref = R.softmax(x, width, queries, 0.125, bool(causal))
+        assert np.all(np.isfinite(ref)) and np.all(ref[:, :130] == 0.0)
+        got = run_softmax(x, rows, width, queries, causal, 0.125, width + 1)
+        assert not np.any(np.isnan(got)), f"width {width}: NaN"
+        check_softmax(got, ref, width)
+
+
 def test_softmax_attention_scores_full_size():
     """8 sequences x 8 heads x 512 queries over 512 keys, scale 1/8 (head size
     64): the scores of the batched attention product, checked on sampled rows."""
