@@ -46,6 +46,9 @@ ABLATIONS = {
     # MFMA kernel, 256 x 128 tile, one running accumulator instead of chunked
     # sums (misses the 1e-6 error bound: what the chunking costs)
     "nochunk": ["-DGEMM_MFMA_HUGE_CONFIG=256,128,32,4,2,2,8,1,1,1,3,0,1,0,1"],
+    # race detection: every stage buffer holds NaN between its release and
+    # its refill (FP32 MFMA, 256 x 256 and packed bf16 kernels; same results)
+    "poison": ["-DGEMM_LDS_POISON=1"],
 }
 
 

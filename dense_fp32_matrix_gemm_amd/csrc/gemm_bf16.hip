@@ -156,14 +156,19 @@ bf16_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     using SA = Stage<Cfg, BM, A_KC>;
     using SB = Stage<Cfg, BN, B_KC>;
     constexpr int kTileA = BM * LD, kTileB = BN * LD;
-    __shared__ __attribute__((aligned(16))) __bf16 lds0[kTileA + kTileB];
-    __shared__ __attribute__((aligned(16))) __bf16 lds1[kTileA + kTileB];
+    // Both stage buffers in one array, so that an LDS address in one buffer
+    // and the same position in the other differ by a constant the compiler
+    // can fold into the instruction's offset.
+    __shared__ __attribute__((aligned(16))) __bf16 lds_both[2 * (kTileA + kTileB)];
+    __bf16 *const lds0 = lds_both;
+    __bf16 *const lds1 = lds_both + kTileA + kTileB;
 
     int tm, tn;
     tile_of<Cfg::GROUP_M>(tile_base + int(blockIdx.x), tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const bool inside = (m0 + BM <= M) && (n0 + BN <= N);
     const int wave = int(threadIdx.x) / kWave, lane = int(threadIdx.x) % kWave;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same, in a scalar register
     const int wm = (wave / Cfg::WAVES_N) * Cfg::WM, wn = (wave % Cfg::WAVES_N) * Cfg::WN;
     const int half = lane / 32, l32 = lane % 32;
 
@@ -246,15 +251,21 @@ bf16_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     }
 
     // Lane l of a 32 x 32 block holds column l % 32 and, in accumulator slot
-    // v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.
+    // v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.  The lane's position is
+    // derived afresh (lane index from the full execution mask, wave index
+    // from a scalar register), so nothing lane-dependent has to stay in a
+    // vector register across the k loop.
+    const int e_lane = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+    const int e_wm = (wave_s / Cfg::WAVES_N) * Cfg::WM, e_wn = (wave_s % Cfg::WAVES_N) * Cfg::WN;
+    const int e_l32 = e_lane % 32, e_half = e_lane / 32;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn + 32 * j + l32;
+            const int col = n0 + e_wn + 32 * j + e_l32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm + 32 * i + 8 * (v / 4) + 4 * half + (v % 4);
+                const int row = m0 + e_wm + 32 * i + 8 * (v / 4) + 4 * e_half + (v % 4);
                 if (inside || (row < M && col < N)) C[int64_t(row) * ldc + col] = acc[i][j][v];
             }
         }

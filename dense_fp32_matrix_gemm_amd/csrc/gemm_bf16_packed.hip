@@ -129,6 +129,12 @@ struct Tile {
     __device__ static __forceinline__ void dma(char *lds, const char *origin,
                                                const uint32_t (&off)[dma_per_wave], int wave)
     {
+        if (GEMM_LDS_POISON) {
+#pragma unroll
+            for (int q = 0; q < dma_per_wave; ++q)
+                poison16(lds + 1024 * (wave * dma_per_wave + q) + 16 * (threadIdx.x % kWave));
+            poison_wait();
+        }
 #pragma unroll
         for (int q = 0; q < dma_per_wave; ++q)
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(origin + off[q]),
@@ -169,6 +175,15 @@ struct Tile {
         for (int q = 0; q < per_thread; ++q) {
             const int i = int(threadIdx.x) + Cfg::threads * q;
             *reinterpret_cast<v4u *>(lds + 16 * slot(i / vpr, i % vpr)) = reg[q];
+        }
+    }
+    // The race-detection build's NaN over the bytes store() will write.
+    __device__ static __forceinline__ void poison(char *lds)
+    {
+#pragma unroll
+        for (int q = 0; q < per_thread; ++q) {
+            const int i = int(threadIdx.x) + Cfg::threads * q;
+            poison16(lds + 16 * slot(i / vpr, i % vpr));
         }
     }
 
@@ -349,6 +364,12 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
             char *cur = (s & 1) ? buf1 : buf0;
             char *nxt = (s & 1) ? buf0 : buf1;
             if (s + 1 < stages) {
+                // nxt was released by the barrier that ended stage s - 1
+                if (GEMM_LDS_POISON) {
+                    TA::poison(nxt);
+                    TB::poison(nxt + TA::bytes);
+                    poison_wait();
+                }
                 TA::template load<VEC>(A, lda, M, K, m0, (s + 1) * BK, ra);
                 TB::template load<VEC>(B, ldb, N, K, n0, (s + 1) * BK, rb);
             }

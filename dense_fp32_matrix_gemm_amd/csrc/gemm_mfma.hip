@@ -205,12 +205,20 @@ struct Tile {
 
     // Registers -> LDS for the register-staged path (same slice-to-thread
     // map as the load).
-    __device__ static __forceinline__ void store(float *lds, const v4f (&reg)[per_thread])
+    __device__ static __forceinline__ void store(float *lds, const v4f (&reg)[per_thread],
+                                                 int tid = int(threadIdx.x))
     {
 #pragma unroll
         for (int q = 0; q < per_thread; ++q)
-            if (Load::active(q))
-                *reinterpret_cast<v4f *>(lds + 4 * slot(Load::row(q), Load::col(q) / 4)) = reg[q];
+            if (Load::active(q, tid))
+                *reinterpret_cast<v4f *>(lds + 4 * slot(Load::row(q, tid), Load::col(q, tid) / 4)) = reg[q];
+    }
+    // The race-detection build's NaN over the bytes store() will write.
+    __device__ static __forceinline__ void poison(float *lds)
+    {
+#pragma unroll
+        for (int q = 0; q < per_thread; ++q)
+            if (Load::active(q)) poison16(lds + 4 * slot(Load::row(q), Load::col(q) / 4));
     }
 
     // Byte offset, from the stage's stored origin, of the vector this lane
@@ -229,6 +237,12 @@ struct Tile {
     __device__ static __forceinline__ void dma(float *lds, const char *origin,
                                                const uint32_t (&off)[dma_per_wave], int wave)
     {
+        if (GEMM_LDS_POISON) {
+#pragma unroll
+            for (int q = 0; q < dma_per_wave; ++q)
+                if (dma_active(wave, q)) poison16(lds + (wave * dma_per_wave + q) * 256 + 4 * (threadIdx.x % kWave));
+            poison_wait();
+        }
 #pragma unroll
         for (int q = 0; q < dma_per_wave; ++q)
             if (dma_active(wave, q))
@@ -284,6 +298,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const int m0 = tm * BM, n0 = tn * BN;
     const bool inside = (m0 + BM <= M) && (n0 + BN <= N);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same, in a scalar register
     const int kslice = wave / Cfg::waves_mn, wmn = wave % Cfg::waves_mn;
     const int wm = (wmn / Cfg::waves_n) * Cfg::WM, wn = (wmn % Cfg::waves_n) * Cfg::WN;
     const int half = lane / 32, l32 = lane % 32;
@@ -320,9 +335,13 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     // fragment reads of k group write_g (the register-staged path writes the
     // next stage there; the buffer it writes was last read in the previous
     // stage, which every wave finished before that stage's barrier).
-    auto compute = [&](const float *lds, auto mid, auto fresh_t, auto fold_t) {
+    // PREFETCH_T: read the next group's fragments ahead (the copy path; the
+    // register-staged path, whose loaded stage is live across the MFMAs,
+    // reads them just in time to stay within the register budget).
+    auto compute = [&](const float *lds, auto mid, auto fresh_t, auto fold_t, auto prefetch_t) {
         constexpr bool kFresh = decltype(fresh_t)::value;
         constexpr bool kFold = decltype(fold_t)::value;
+        constexpr bool kPrefetch = Cfg::prefetch && decltype(prefetch_t)::value && !(Cfg::BM == 256 && !A_KC && B_KC);
         const float *la = lds;
         const float *lb = lds + TA::floats;
         constexpr int kGroups = BK / 8 / Cfg::ksplit;  // k groups per slice per stage
@@ -336,12 +355,12 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #pragma unroll
             for (int j = 0; j < FN; ++j) fb[slot][j] = TB::fragment(lb, wn + j * kBlk + l32, g, half);
         };
-        if (Cfg::prefetch) read(0, 0);
+        if (kPrefetch) read(0, 0);
         if constexpr (Cfg::prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < kGroups; ++t) {
-            const int cur = Cfg::prefetch ? (t & 1) : 0;
-            if (!Cfg::prefetch)
+            const int cur = kPrefetch ? (t & 1) : 0;
+            if (!kPrefetch)
                 read(t, 0);
             else if (t + 1 < kGroups)
                 read(t + 1, (t + 1) & 1);
@@ -361,7 +380,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             // With prefetch, ask the scheduler to spread the next group's LDS
             // reads between this group's MFMAs (one read, then an even share
             // of the MFMAs) instead of clustering them: +0.5-1.5 %.
-            if (Cfg::prefetch && t + 1 < kGroups) {
+            if (kPrefetch && t + 1 < kGroups) {
                 constexpr int kReads = TA::reads * FM + TB::reads * FN;
                 constexpr int kMfma = 4 * FM * FN;
                 constexpr int per = kMfma / kReads > 0 ? kMfma / kReads : 1;
@@ -393,6 +412,12 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             float *cur = (s & 1) ? buf1 : buf0;
             float *nxt = (s & 1) ? buf0 : buf1;
             if (s + 1 < stages) {
+                // nxt was released by the barrier that ended stage s - 1
+                if (GEMM_LDS_POISON) {
+                    TA::poison(nxt);
+                    TB::poison(nxt + TA::floats);
+                    poison_wait();
+                }
                 v4f ra[TA::per_thread], rb[TB::per_thread];
                 const int k = (s + 1) * BK;
                 TA::Load::template load<true, VEC>(opa, a_r(k), a_c(k), ra);
@@ -400,9 +425,9 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                 compute(cur, [&] {
                     TA::store(nxt, ra);
                     TB::store(nxt + TA::floats, rb);
-                }, Yes{}, Yes{});
+                }, Yes{}, Yes{}, No{});
             } else {
-                compute(cur, nothing, Yes{}, Yes{});
+                compute(cur, nothing, Yes{}, Yes{}, No{});
             }
             __syncthreads();
         }
@@ -450,7 +475,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                     // buffer -- copy, barrier, compute, barrier, next copy.
                     wait_vm<0>();
                     __syncthreads();
-                    compute(buf0, nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{});
+                    compute(buf0, nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{}, Yes{});
                     __syncthreads();
                     if (st + 1 < full) dma(buf0, st + 1);
                 } else if (st < full) {
@@ -470,21 +495,26 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                     if (!late && st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
                     compute(bufp(Int<b % NB>{}), [&] {
                         if (late && st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
-                    }, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{});
+                    }, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{}, Yes{});
                 }
             });
         }
         if (full % FOLD != 0) fold_part();  // the last chunk was cut short
         __syncthreads();  // every wave is done with the last full stage's buffer
         if (full < stages) {
-            // The partial last stage, predicated, through registers.
+            // The partial last stage, predicated, through registers.  Its
+            // thread index is derived afresh (the lane counted from the full
+            // execution mask, the wave from a scalar register) and its
+            // fragments are read as in the loop, so that nothing besides the
+            // accumulators has to stay live across the loop for it.
+            const int tid = kWave * wave_s + int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
             v4f ra[TA::per_thread], rb[TB::per_thread];
-            TA::Load::template load<true, VEC>(opa, a_r(full * BK), a_c(full * BK), ra);
-            TB::Load::template load<true, VEC>(opb, b_r(full * BK), b_c(full * BK), rb);
-            TA::store(buf0, ra);
-            TB::store(buf0 + TA::floats, rb);
+            TA::Load::template load<true, VEC>(opa, a_r(full * BK), a_c(full * BK), ra, tid);
+            TB::Load::template load<true, VEC>(opb, b_r(full * BK), b_c(full * BK), rb, tid);
+            TA::store(buf0, ra, tid);
+            TB::store(buf0 + TA::floats, rb, tid);
             __syncthreads();
-            compute(buf0, nothing, Yes{}, Yes{});
+            compute(buf0, nothing, Yes{}, Yes{}, Yes{});
             __syncthreads();
         }
     } else {
@@ -533,16 +563,23 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     // Epilogue.  Lane l of a 32 x 32 block holds column l % 32 and, in
     // accumulator slot v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.  The fused
     // variant adds bias[column] and applies the activation before the store
-    // (both flags are uniform over the launch).
+    // (both flags are uniform over the launch).  The lane's position is
+    // derived afresh -- the lane index counted from the (full) execution
+    // mask, the wave index from a scalar register -- so that nothing
+    // lane-dependent has to stay in a vector register across the k loop.
+    const int e_lane = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+    const int e_wmn = wave_s % Cfg::waves_mn;
+    const int e_wm = (e_wmn / Cfg::waves_n) * Cfg::WM, e_wn = (e_wmn % Cfg::waves_n) * Cfg::WN;
+    const int e_l32 = e_lane % 32, e_half = e_lane / 32;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn + j * kBlk + l32;
+            const int col = n0 + e_wn + j * kBlk + e_l32;
             const float bj = (bias != nullptr && col < N) ? bias[col] : 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm + i * kBlk + 8 * (v / 4) + 4 * half + (v % 4);
+                const int row = m0 + e_wm + i * kBlk + 8 * (v / 4) + 4 * e_half + (v % 4);
                 float x = acc[i][j][v] + bj;
                 if (act == 1) x = gelu(x);
                 if (inside || (row < M && col < N)) {
@@ -648,7 +685,10 @@ void dispatch(const Problem &p, hipStream_t s)
 template <class Cfg, bool A_KC, bool B_KC>
 void dispatch_vec(const Problem &p, hipStream_t s)
 {
-    if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
+    // Product b reads A + b * stride_a and B + b * stride_b, so in a batch
+    // the strides must keep every product's operands 16-byte aligned too.
+    const bool strides_ok = p.batch <= 1 || (p.stride_a % kVec == 0 && p.stride_b % kVec == 0);
+    if (strides_ok && vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
         dispatch<Cfg, A_KC, B_KC, true>(p, s);
     else
         dispatch<Cfg, A_KC, B_KC, false>(p, s);

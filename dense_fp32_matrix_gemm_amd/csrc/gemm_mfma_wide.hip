@@ -155,6 +155,13 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
     auto copy_stage = [&](float *dst, int st) {
         const char *sa = ga + st * a_step;
         const char *sb = gb + st * b_step;
+        if (GEMM_LDS_POISON) {
+#pragma unroll
+            for (int q = 0; q < kAPieces; ++q) poison16(dst + (wave * kAPieces + q) * 256 + 4 * lane);
+#pragma unroll
+            for (int q = 0; q < kBPieces; ++q) poison16(dst + kAFloats + (wave * kBPieces + q) * 256 + 4 * lane);
+            poison_wait();
+        }
 #pragma unroll
         for (int q = 0; q < kAPieces; ++q)
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(sa + oa[q]),

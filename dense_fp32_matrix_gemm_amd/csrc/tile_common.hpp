@@ -33,11 +33,16 @@ struct Slice {
     static_assert(vecs % THREADS == 0 || THREADS % vecs == 0,
                   "a slice splits evenly over the block, or covers part of it");
 
-    __device__ static __forceinline__ int index(int q) { return int(threadIdx.x) + THREADS * q; }
+    // tid: the thread's index in the block (threadIdx.x, or the same value
+    // derived afresh where the caller wants it recomputed rather than kept).
+    __device__ static __forceinline__ int index(int q, int tid) { return tid + THREADS * q; }
     // False only for the threads past the end of a slice smaller than the block.
-    __device__ static __forceinline__ bool active(int q) { return vecs % THREADS == 0 || index(q) < vecs; }
-    __device__ static __forceinline__ int row(int q) { return index(q) / vec_per_row; }
-    __device__ static __forceinline__ int col(int q) { return (index(q) % vec_per_row) * 4; }
+    __device__ static __forceinline__ bool active(int q, int tid) { return vecs % THREADS == 0 || index(q, tid) < vecs; }
+    __device__ static __forceinline__ int row(int q, int tid) { return index(q, tid) / vec_per_row; }
+    __device__ static __forceinline__ int col(int q, int tid) { return (index(q, tid) % vec_per_row) * 4; }
+    __device__ static __forceinline__ bool active(int q) { return active(q, int(threadIdx.x)); }
+    __device__ static __forceinline__ int row(int q) { return row(q, int(threadIdx.x)); }
+    __device__ static __forceinline__ int col(int q) { return col(q, int(threadIdx.x)); }
 
     // Load the slice whose stored origin is (r0, c0).  CHECK: elements
     // outside rows_total x cols_total read as zero and are never
@@ -46,14 +51,20 @@ struct Slice {
     template <bool CHECK, bool VEC>
     __device__ static __forceinline__ void load(const Operand &op, int r0, int c0, v4f (&reg)[per_thread])
     {
+        load<CHECK, VEC>(op, r0, c0, reg, int(threadIdx.x));
+    }
+    template <bool CHECK, bool VEC>
+    __device__ static __forceinline__ void load(const Operand &op, int r0, int c0, v4f (&reg)[per_thread],
+                                                int tid)
+    {
 #pragma unroll
         for (int q = 0; q < per_thread; ++q) {
-            if (!active(q)) {
+            if (!active(q, tid)) {
                 reg[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
                 continue;
             }
-            const int r = r0 + row(q);
-            const int c = c0 + col(q);
+            const int r = r0 + row(q, tid);
+            const int c = c0 + col(q, tid);
             const float *src = op.base + int64_t(r) * op.ld + c;
             if (!CHECK) {
                 if (VEC) {
@@ -88,6 +99,33 @@ __device__ __forceinline__ void wait_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// GEMM_LDS_POISON 1 builds the race-detection ablation (the library is built
+// with 0): before a stage buffer is refilled, each lane first writes NaN
+// over exactly the LDS bytes its own copies (or stores) of the refill will
+// fill, and waits until those writes are done.  The buffer then holds NaN
+// from the moment the barrier releases it until the refill lands, so a wave
+// that reads it too early (a missing wait) or still reads the previous
+// stage after the release (a missing barrier) multiplies NaN, which reaches
+// C.  Results are otherwise unchanged.
+#ifndef GEMM_LDS_POISON
+#define GEMM_LDS_POISON 0
+#endif
+
+// Write NaN over the 16 bytes at `lds` (poison build only).
+__device__ __forceinline__ void poison16(void *lds)
+{
+    if (GEMM_LDS_POISON) {
+        const float q = __builtin_nanf("");
+        *reinterpret_cast<v4f *>(lds) = v4f{q, q, q, q};
+    }
+}
+// Wait until this wave's LDS writes are done (poison build only): vmcnt and
+// expcnt left at their maxima, lgkmcnt 0.
+__device__ __forceinline__ void poison_wait()
+{
+    if (GEMM_LDS_POISON) __builtin_amdgcn_s_waitcnt(0xC07F);
 }
 
 // Workgroup index -> (tile row, tile column) of a tiles_m x tiles_n grid.

@@ -83,6 +83,25 @@ def test_integer_exact_batched(ta, tb, gap, shared, shape):
         P.check_exact(got[b], ref[b], f"{w.name}[{b}] t{ta}{tb} gap{gap} shared{shared}")
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("gap", [1, 3])
+def test_integer_exact_batched_aligned_ld_odd_stride(ta, tb, gap):
+    """Leading dimensions that are multiples of 4 with strides that are not:
+    product 0 is 16-byte aligned, products 1.. are not, so every product must
+    take the element-wise loads.  Exact against the oracle."""
+    M, N, K, batch = 136, 200, 72, 5
+    w = gi.Workload(f"b{M}x{N}x{K}a", M, N, K, 91, 92, "int8", "int8", ta, tb,
+                    lda=(M if ta else K) + 4, ldb=(K if tb else N) + 8, ldc=N + 4,
+                    batch=batch, gap=gap)
+    assert w.lda_ % 4 == 0 and w.ldb_ % 4 == 0 and w.stride_a % 4 != 0 and w.stride_b % 4 != 0
+    A, B = w.make_a(), w.make_b()
+    got, pad = split_c(w, run_batched(w, A, B, w.make_c()))
+    assert np.all(pad == np.float32(gi.OUTPUT_PAD))
+    ref = reference(w, A, B)
+    for b in range(batch):
+        P.check_exact(got[b], ref[b], f"{w.name}[{b}] t{ta}{tb} gap{gap}")
+
+
 def test_batch_zero_and_k_zero():
     w = gi.Workload("kz", 20, 30, 0, 1, 2, transB=0, batch=3, gap=2, lda=1, ldb=30)
     A = np.full((3, 20 * 1 + 2), np.nan, np.float32)
