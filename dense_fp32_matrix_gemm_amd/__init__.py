@@ -17,6 +17,7 @@ from __future__ import annotations
 from ._lib import (ACT_GELU, ACT_NONE, ALGOS, PLANS, LibraryNotBuilt, gemm_f32, gemm_f32_bf16,
                    gemm_f32_bf16_packed, gemm_f32_bias_act, gemm_f32_pack_bf16,
                    gemm_f32_ex, gemm_f32_naive, gemm_f32_plan, gemm_f32_splitk,
+                   gemm_f32_splitk_noalloc,
                    gemm_f32_splitk_workspace_size,
                    gemm_f32_strerror, gemm_f32_strided_batched, gemm_f32_version, library_path,
                    load, rows_normalize_backward_f32, rows_normalize_f32,
@@ -25,7 +26,8 @@ from ._lib import (ACT_GELU, ACT_NONE, ALGOS, PLANS, LibraryNotBuilt, gemm_f32, 
 __all__ = ["ACT_GELU", "ACT_NONE", "ALGOS", "PLANS", "GemmError", "LibraryNotBuilt", "bmm", "gemm_f32",
            "gemm_f32_bf16", "gemm_f32_bf16_packed", "gemm_f32_bias_act", "gemm_f32_ex",
            "gemm_f32_pack_bf16", "linear", "matmul_bf16", "matmul_bf16_packed", "pack_bf16",
-           "gemm_f32_naive", "gemm_f32_plan", "gemm_f32_splitk", "gemm_f32_splitk_workspace_size",
+           "gemm_f32_naive", "gemm_f32_plan", "gemm_f32_splitk", "gemm_f32_splitk_noalloc",
+           "gemm_f32_splitk_workspace_size",
            "gemm_f32_strerror", "gemm_f32_strided_batched",
            "gemm_f32_version", "library_path", "load", "matmul", "matmul_splitk",
            "normalize", "normalize_backward", "operand_layout", "rows_normalize_backward_f32",

@@ -40,6 +40,8 @@ SIGNATURES = {
     "gemm_f32_bf16_packed": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr]),
     "gemm_f32_splitk": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _int,
                                _i64, _ptr, _i64, _ptr]),
+    "gemm_f32_splitk_noalloc": (_int, [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int,
+                                       _int, _i64, _ptr]),
     "gemm_f32_splitk_workspace_size": (_i64, [_i64, _i64, _i64, _i64]),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
     "rows_softmax_f32": (_int, [_i64, _i64, _i64, _int, _flt, _ptr, _i64, _ptr, _i64, _ptr]),
@@ -135,6 +137,18 @@ def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, splits, wor
     ``gemm_f32_splitk_workspace_size`` bytes (0/None when that is 0)."""
     return _call("gemm_f32_splitk", M, N, K, A, lda, B, ldb, C, ldc, transA, transB, splits,
                  workspace, workspace_bytes, stream)
+
+
+# GEMM_F32_SPLITK_SCRATCH_BYTES: the partial products gemm_f32_splitk_noalloc holds
+SPLITK_SCRATCH_BYTES = 64 << 20
+
+
+def gemm_f32_splitk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, transA, transB, splits,
+                            stream) -> int:
+    """gemm_f32_splitk with the partials in the library's own per-GPU scratch
+    (at most SPLITK_SCRATCH_BYTES); allocates nothing."""
+    return _call("gemm_f32_splitk_noalloc", M, N, K, A, lda, B, ldb, C, ldc, transA, transB,
+                 splits, stream)
 
 
 def gemm_f32_splitk_workspace_size(M, N, K, splits) -> int:

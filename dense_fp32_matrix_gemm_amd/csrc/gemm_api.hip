@@ -7,6 +7,7 @@
 #include "gemm_internal.hpp"
 
 #include <climits>
+#include <mutex>
 
 namespace {
 
@@ -53,6 +54,70 @@ int64_t splitk_used(int64_t K, int64_t splits)
 {
     const int64_t len = splitk_len(K, splits);
     return (K + len - 1) / len;
+}
+
+// Device memory of gemm_f32_splitk_noalloc: the split-k partial products of
+// callers that cannot allocate.  Each GPU the library runs on holds its own
+// copy until the process ends, and every call on that GPU shares it.  In
+// host code `scratch` names a host-side stand-in, never the device array:
+// host code uses only the address hipGetSymbolAddress returns for it.
+static __device__ __align__(256) float scratch[GEMM_F32_SPLITK_SCRATCH_BYTES / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_lock;
+float *scratch_addr[kMaxDevices];  // per device, filled on its first call
+
+// The device address of `scratch` on the GPU that runs `stream` (the
+// current device for the null stream), looked up once per device with that
+// device current.
+hipError_t scratch_on(hipStream_t stream, float **out)
+{
+    int dev = 0;
+    hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(scratch_lock);
+    if (scratch_addr[dev] == nullptr) {
+        int cur = 0;
+        if ((err = hipGetDevice(&cur)) != hipSuccess) return err;
+        if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return err;
+        void *addr = nullptr;
+        err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess) return err;
+        if (addr == nullptr) return hipErrorInvalidSymbol;
+        scratch_addr[dev] = static_cast<float *>(addr);
+    }
+    *out = scratch_addr[dev];
+    return hipSuccess;
+}
+
+// The split-k launches for a validated problem with s_used > 1: the partial
+// products into ws (s_used packed M x N slices), then their fixed-order sum
+// into C.
+hipError_t launch_splitk(Problem p, int64_t K, int64_t splits, float *ws, hipStream_t s)
+{
+    // Partial s reads op(A)[:, s*len ..] and op(B)[s*len .., :]: a run of k
+    // moves along the stored rows of an operand whose rows hold k (A
+    // untransposed, B transposed), else down its rows.
+    float *C = p.C;
+    const int64_t ldc = p.ldc;
+    const int64_t len = splitk_len(K, splits);
+    const int64_t used = splitk_used(K, splits);
+    p.K = int(len);
+    p.k_total = int(K);
+    p.stride_a = p.transA ? len * p.lda : len;
+    p.stride_b = p.transB ? len : len * p.ldb;
+    p.C = ws;
+    p.ldc = p.N;
+    p.stride_c = int64_t(p.M) * p.N;
+    p.batch = used;
+    hipError_t err = gemmf32::launch_mfma(p, s, 0);
+    if (err == hipSuccess) err = gemmf32::launch_splitk_reduce(ws, int(used), p.M, p.N, C, ldc, s);
+    return err;
 }
 
 int run(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
@@ -132,6 +197,8 @@ const char *gemm_f32_strerror(int status)
     case -kArgTransA: return "invalid argument 10 (transA): not 0 or 1";
     case -kArgTransB: return "invalid argument 11 (transB): not 0 or 1";
     case -12: return "invalid argument 12 (gemm_f32_splitk: splits < 1 or too large a workspace; "
+                     "gemm_f32_splitk_noalloc: the same, or partial products larger than "
+                     "GEMM_F32_SPLITK_SCRATCH_BYTES (use fewer splits); "
                      "gemm_f32_strided_batched: strideC negative or overlapping)";
     case -kArgAlgo: return "invalid argument 13 (gemm_f32_ex: unknown kernel family; gemm_f32_bias_act: "
                            "unknown activation; gemm_f32_splitk: workspace NULL; "
@@ -285,22 +352,34 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda
         const hipError_t err = gemmf32::launch_mfma(p, s, 0);
         return err == hipSuccess ? 0 : int(err);
     }
-    // Partial s reads op(A)[:, s*len ..] and op(B)[s*len .., :]: a run of k
-    // moves along the stored rows of an operand whose rows hold k (A
-    // untransposed, B transposed), else down its rows.
-    const int64_t len = splitk_len(K, splits);
-    const int64_t used = splitk_used(K, splits);
-    p.K = int(len);
-    p.k_total = int(K);
-    p.stride_a = transA ? len * lda : len;
-    p.stride_b = transB ? len : len * ldb;
-    p.C = workspace;
-    p.ldc = N;
-    p.stride_c = M * N;
-    p.batch = used;
-    hipError_t err = gemmf32::launch_mfma(p, s, 0);
-    if (err == hipSuccess)
-        err = gemmf32::launch_splitk_reduce(workspace, int(used), int(M), int(N), C, ldc, s);
+    const hipError_t err = launch_splitk(p, K, splits, workspace, s);
+    return err == hipSuccess ? 0 : int(err);
+}
+
+int gemm_f32_splitk_noalloc(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                            const float *B, int64_t ldb, float *C, int64_t ldc, int transA,
+                            int transB, int64_t splits, void *stream)
+{
+    const int bad = validate(M, N, K, A, lda, B, ldb, C, ldc, transA, transB);
+    if (bad) return bad;
+    const int64_t need = gemm_f32_splitk_workspace_size(M, N, K, splits);
+    if (need < 0) return int(need);
+    if (need > GEMM_F32_SPLITK_SCRATCH_BYTES) return -12;  // more partials than the scratch holds
+    if (M == 0 || N == 0) return 0;
+    const Problem p{int(M), int(N), int(K), A, lda, B, ldb, C, ldc, transA, transB};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (K == 0) {
+        err = gemmf32::launch_zero_fill(p, s);
+    } else if (need == 0) {
+        err = gemmf32::launch_mfma(p, s, 0);
+    } else {
+        // Every element of each partial is written before the sum reads it,
+        // so the scratch needs no clearing between calls.
+        float *ws = nullptr;
+        err = scratch_on(s, &ws);
+        if (err == hipSuccess) err = launch_splitk(p, K, splits, ws, s);
+    }
     return err == hipSuccess ? 0 : int(err);
 }
 

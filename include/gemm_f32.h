@@ -24,7 +24,8 @@
  *
  * Pointers and ownership: A, B and C are DEVICE pointers owned by the caller.
  * The library allocates, frees and copies nothing, keeps no state between
- * calls and never synchronises: each call enqueues its kernels on `stream`
+ * calls (gemm_f32_splitk_noalloc's per-GPU scratch array aside) and never
+ * synchronises: each call enqueues its kernels on `stream`
  * (a hipStream_t passed as void*; NULL means the default stream) and
  * returns; C is complete when the stream reaches that point.  C must not
  * overlap A or B.  Concurrent calls on different streams are safe.
@@ -252,6 +253,33 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
                     float *C, int64_t ldc,
                     int transA, int transB, int64_t splits,
                     float *workspace, int64_t workspace_bytes, void *stream);
+
+/* The largest partial products, in bytes (s_used*M*N*4), that
+ * gemm_f32_splitk_noalloc holds: 64 MiB of device memory per GPU. */
+#define GEMM_F32_SPLITK_SCRATCH_BYTES (64LL << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc:
+ * gemm_f32_splitk without a workspace argument.  The partial products go to
+ * a scratch array of GEMM_F32_SPLITK_SCRATCH_BYTES that the library keeps in
+ * each GPU's memory (reserved when the library's code is first loaded on
+ * that GPU and held until the process ends); the call itself allocates and
+ * frees nothing.  Same arithmetic, results and codes as gemm_f32_splitk with
+ * the same splits (bit for bit), arguments 1-12 numbered as there and the
+ * stream as argument 13; -12 also when s_used*M*N*4 exceeds
+ * GEMM_F32_SPLITK_SCRATCH_BYTES (fewer splits fit; splits = 1 always does).
+ * Every call on one GPU shares that GPU's scratch array: calls that overlap
+ * in time on the same GPU (on different streams, or from different host
+ * threads without stream ordering) race and give wrong results; calls
+ * ordered on one stream are safe.  Nothing needs clearing between calls
+ * (each partial is written whole before it is summed).  The stream's GPU
+ * must be the one that owns C; its scratch address is looked up on its
+ * first call (a positive hipError_t if that fails). */
+int gemm_f32_splitk_noalloc(int64_t M, int64_t N, int64_t K,
+                            const float *A, int64_t lda,
+                            const float *B, int64_t ldb,
+                            float *C, int64_t ldc,
+                            int transA, int transB, int64_t splits, void *stream);
 
 /* Bytes of workspace gemm_f32_splitk needs for these sizes: s_used*M*N*4,
  * or 0 when it runs as a single product.  Negative (-1, -2, -3, -12) for an

@@ -255,6 +255,39 @@ def test_splitk_quick_return_without_launch():
     assert splitk(M=0, ws=None, ws_bytes=0) == 0
 
 
+def noalloc(M=8, N=8, K=64, splits=2, **kw):
+    return g.gemm_f32_splitk_noalloc(M, N, K, kw.get("A", FAKE), kw.get("lda", max(K, 1)),
+                                     kw.get("B", FAKE), kw.get("ldb", max(N, 1)),
+                                     kw.get("C", FAKE), kw.get("ldc", max(N, 1)),
+                                     kw.get("ta", 0), kw.get("tb", 0), splits, None)
+
+
+def test_splitk_noalloc_argument_errors():
+    """Checked on the host before the scratch lookup or any launch."""
+    assert noalloc(splits=0) == -12 and noalloc(splits=-1) == -12
+    assert noalloc(M=-1) == -1 and noalloc(N=-2) == -2 and noalloc(K=-3) == -3
+    assert noalloc(lda=3) == -5 and noalloc(ldb=7) == -7 and noalloc(ldc=7) == -9
+    assert noalloc(C=None) == -8 and noalloc(ta=2) == -10 and noalloc(tb=-1) == -11
+    # the largest partial products the scratch holds, and one float more
+    cap = _lib.SPLITK_SCRATCH_BYTES
+    assert g.gemm_f32_splitk_workspace_size(1024, 4096, 8192, 4) == cap
+    assert noalloc(M=1025, N=4096, K=8192, splits=4, lda=8192, ldb=4096, ldc=4096) == -12
+    assert noalloc(M=4096, N=4096, K=4096, splits=2, lda=4096, ldb=4096, ldc=4096) == -12
+    assert "SCRATCH" in g.gemm_f32_strerror(-12)
+
+
+def test_splitk_noalloc_quick_returns_without_launch():
+    assert noalloc(M=0) == 0 and noalloc(N=0) == 0
+    # an empty output needs no partials, so no scratch limit applies
+    assert noalloc(M=0, N=4096, K=8192, splits=4, lda=8192, ldb=4096, ldc=4096) == 0
+
+
+def test_splitk_noalloc_scratch_limit_in_header():
+    text = open(os.path.join(ROOT, "include", "gemm_f32.h")).read()
+    m = re.search(r"#define GEMM_F32_SPLITK_SCRATCH_BYTES \((\d+)LL << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.SPLITK_SCRATCH_BYTES
+
+
 # --------------------------------------------------------- row reductions ---
 
 def test_rows_header_is_plain_c():
