@@ -590,12 +590,24 @@ def main(argv=None) -> int:
                 "traffic": read_traffic(kernel, name),
                 "kernel": kernel, "flops_per_launch": flops,
                 "compulsory_bytes": compulsory_bytes(w.M, w.N, w.K) * w.batch}
+    roofline["peak_basis"] = ("dense bf16 matrix-core peak, published" if mixed else
+                              "FP32 MFMA: 256 flop/clk/CU x 256 CUs x 2.4 GHz")
     if args.algo == "naive":
         model = naive_model_bytes(w.M, w.N, w.K) / (ms * 1e-3) / 1e9
         roofline.update(bound="hbm", achieved=model, peak=MI355X_HBM_TBPS * 1000,
-                        unit="GB/s", frac=model / (MI355X_HBM_TBPS * 1000))
+                        unit="GB/s", frac=model / (MI355X_HBM_TBPS * 1000),
+                        peak_basis="the pages' naive model: every operand read from HBM at 8.0 TB/s, "
+                                   "8 bytes per multiply-add (1/4 flop per byte)",
+                        measured_limiter="load latency: each wave waits for its k-th loads before the "
+                                         "next, one load in flight per wave (profiles/naive_S4k.md)")
     elif args.algo == "fma":
-        roofline["bound"] = "alu"   # vector FP32 FMA; same 157.3 TFLOP/s peak as the matrix cores
+        # The kernel issues plain v_fmac_f32 (packed FP32 is disabled in every
+        # build); gfx950 completes one wave64 v_fmac_f32 per 2 cycles per SIMD,
+        # so its peak is 64 lanes x 2 flop / 2 cycles x 4 SIMDs x 256 CUs x
+        # 2.4 GHz, the same 157.3 TFLOP/s (the kernel's own counters show more
+        # than one instruction per 4 cycles per SIMD).
+        roofline.update(bound="alu", peak_basis="plain v_fmac_f32 (VOP2): one wave64 instruction per "
+                        "2 cycles per SIMD, 64 x 2 flop / 2 x 4 SIMDs x 256 CUs x 2.4 GHz")
 
     context = None
     vendor_host = None  # torch.mm's result, for the accuracy comparison

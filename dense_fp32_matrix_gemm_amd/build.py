@@ -42,6 +42,7 @@ def sources() -> List[str]:
 ABLATIONS = {
     "noswizzle": ["-DGEMM_MFMA_SWIZZLE=0"],  # MFMA kernel LDS rows without the XOR swizzle
     "nopad": ["-DGEMM_FMA_PAD=0"],           # vector-FMA kernel LDS rows without padding
+    "fmanoswizzle": ["-DGEMM_FMA_SWIZZLE=0"],  # vector-FMA kernel: transposed tiles unswizzled
     "singlebuffer": ["-DGEMM_MFMA_SINGLE_BUFFER=1"],  # MFMA kernel: copy/barrier/compute/barrier
     # MFMA kernel, 256 x 128 tile, one running accumulator instead of chunked
     # sums (misses the 1e-6 error bound: what the chunking costs)

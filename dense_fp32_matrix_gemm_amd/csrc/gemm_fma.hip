@@ -12,7 +12,9 @@
 //  * LDS tiles are k-major, As[k][m] and Bs[k][n] (the page stores A
 //    transposed so a column of A is contiguous).  Operands whose stored rows
 //    run along k are transposed on their way into LDS, four scalar writes per
-//    16-byte global load; rows are padded by 4 floats.
+//    16-byte global load; rows are padded by 4 floats, and the transposed
+//    tiles' 4-float groups are XOR-swizzled by k so those writes spread over
+//    the banks.
 //  * Lane (ty, tx) of the 16 x 16 lane grid owns rows {4ty..4ty+3,
 //    64+4ty..64+4ty+3} and columns {4tx..4tx+3, 64+4tx..64+4tx+3}; its LDS
 //    reads are four 16-byte reads per k, and the 16 lanes sharing a ty read
@@ -33,6 +35,9 @@ constexpr int TM = 8, TN = 8;
 #define GEMM_FMA_PAD 4
 #endif
 constexpr int kPad = GEMM_FMA_PAD;
+#ifndef GEMM_FMA_SWIZZLE
+#define GEMM_FMA_SWIZZLE 1
+#endif
 constexpr int kLd = 128 + kPad;  // LDS row length, both operands (BM == BN)
 constexpr int kGroupM = 8;
 
@@ -43,6 +48,18 @@ struct Stage {
     using Load = Slice<KC ? P : BK, KC ? BK : P, kThreads>;
     static constexpr int per_thread = Load::per_thread;
 
+    // Transposed tiles: row k of the LDS tile holds m (or n) position x at
+    // column x ^ swz(k).  The transposing writes of one wave cover 8
+    // consecutive positions at 8 values of k four apart; with rows of 132
+    // floats, k and k + 16 would land on the same bank, and flipping bit 3
+    // of the position for k >= 16 separates them.  The flip moves whole
+    // 4-float groups, so the 16-byte fragment reads stay contiguous.
+    // GEMM_FMA_SWIZZLE 0 builds the unswizzled ablation (same results).
+    __device__ static __forceinline__ int swz(int k)
+    {
+        return (KC && GEMM_FMA_SWIZZLE) ? ((k >> 4) & 1) << 3 : 0;
+    }
+
     __device__ static __forceinline__ void store(float *lds, const v4f (&reg)[per_thread])
     {
 #pragma unroll
@@ -50,7 +67,7 @@ struct Stage {
             const int r = Load::row(q), c = Load::col(q);
             if (KC) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lds[(c + e) * kLd + r] = reg[q][e];
+                for (int e = 0; e < 4; ++e) lds[(c + e) * kLd + (r ^ swz(c + e))] = reg[q][e];
             } else {
                 *reinterpret_cast<v4f *>(lds + r * kLd + c) = reg[q];
             }
@@ -118,10 +135,11 @@ fma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                 for (int j = 0; j < TN; ++j) part[i][j] = 0.0f;
 #pragma unroll 4
             for (int k = 0; k < BK; ++k) {
-                const v4f a0 = *reinterpret_cast<const v4f *>(la + k * kLd + 4 * ty);
-                const v4f a1 = *reinterpret_cast<const v4f *>(la + k * kLd + 64 + 4 * ty);
-                const v4f b0 = *reinterpret_cast<const v4f *>(lb + k * kLd + 4 * tx);
-                const v4f b1 = *reinterpret_cast<const v4f *>(lb + k * kLd + 64 + 4 * tx);
+                const int sa = SA::swz(k), sb = SB::swz(k);
+                const v4f a0 = *reinterpret_cast<const v4f *>(la + k * kLd + ((4 * ty) ^ sa));
+                const v4f a1 = *reinterpret_cast<const v4f *>(la + k * kLd + ((64 + 4 * ty) ^ sa));
+                const v4f b0 = *reinterpret_cast<const v4f *>(lb + k * kLd + ((4 * tx) ^ sb));
+                const v4f b1 = *reinterpret_cast<const v4f *>(lb + k * kLd + ((64 + 4 * tx) ^ sb));
                 const float a[TM] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
                 const float b[TN] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
 #pragma unroll
