@@ -53,6 +53,19 @@ constexpr int kBPieces = kBFloats / 256 / kWaves;
 constexpr int kGroupM = 4;  // tile-rows per group of the launch order
 constexpr int kWideMaxK = 1024;
 constexpr int kWideMinTiles = kCUs;  // auto selection: at least one tile per CU
+// Products of at most kShortStages stages keep every stage in LDS at once
+// and store the tile in kShortParts column parts (see the kernel).
+constexpr int kShortStages = 2;
+#ifndef GEMM_WIDE_SHORT_PARTS
+#define GEMM_WIDE_SHORT_PARTS 4
+#endif
+constexpr int kShortParts = GEMM_WIDE_SHORT_PARTS;
+#ifndef GEMM_WIDE_SHORT_CHAINS
+#define GEMM_WIDE_SHORT_CHAINS 2
+#endif
+constexpr int kShortChains = GEMM_WIDE_SHORT_CHAINS;
+static_assert(4 % kShortChains == 0, "chains divide the 4 MFMAs of a k group");
+static_assert(kFN % kShortParts == 0, "parts are whole column blocks");
 static_assert(kAPieces * kWaves * 256 == kAFloats && kBPieces * kWaves * 256 == kBFloats,
               "each stage splits into whole 1 KB copies per wave");
 
@@ -186,13 +199,102 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
 #pragma unroll
     for (int j = 0; j < kFN; ++j) jt[j] = OB::block(j, half);
 
+    const int stages = K / kBK;
+    if (stages <= kShortStages) {
+        // Short k (32 or 64: the attention scores over a head of 64): both
+        // stages are copied at once, and the wave's 64 x 128 tile is then
+        // computed in kShortParts parts of whole column blocks.  The stores
+        // of part q - 1 are issued a few at a time between the MFMAs of part
+        // q, so the output leaves while the products run; with only two
+        // stages per tile, storing the whole tile at the end would follow
+        // the products with nothing to overlap it (all workgroups start and
+        // finish together).
+        copy_stage(lds, 0);
+        if (stages > 1) copy_stage(lds + kStage, 1);
+        wait_vm<0>();
+        __syncthreads();
+        constexpr int kCols = kFN / kShortParts;   // 32-column blocks per part
+        constexpr int kStores = kFM * kCols * 16;  // store instructions per part
+        constexpr int kSlots = kShortStages * 4;   // k groups per part
+        constexpr int kPer = (kStores + kSlots - 1) / kSlots;
+        v16f done[kFM][kCols];  // the previous part, bias and activation applied
+        auto put = [&](int q, int s) {
+            const int i = s / (16 * kCols), j = (s / 16) % kCols, v = s % 16;
+            const int col = n0 + wn + 32 * (q * kCols + j) + l32;
+            const int row = m0 + wm + 32 * i + 8 * (v / 4) + 4 * half + (v % 4);
+            __builtin_nontemporal_store(done[i][j][v], &C[int64_t(row) * ldc + col]);
+        };
+#pragma unroll
+        for (int q = 0; q < kShortParts; ++q) {
+            // kShortChains partial sums per block (MFMA u of each k group
+            // feeds sum u % kShortChains), so a wave keeps kShortChains * kFM
+            // * kCols independent MFMA chains in flight
+            v16f part[kFM][kCols][kShortChains];
+#pragma unroll
+            for (int i = 0; i < kFM; ++i)
+#pragma unroll
+                for (int j = 0; j < kCols; ++j)
+#pragma unroll
+                    for (int c = 0; c < kShortChains; ++c) part[i][j][c] = v16f{0.0f};
+#pragma unroll
+            for (int st = 0; st < kShortStages; ++st) {
+                const float *c = lds + st * kStage;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    if (st < stages) {
+                        v4f fa[kFM], fb[kCols];
+#pragma unroll
+                        for (int i = 0; i < kFM; ++i) fa[i] = OA::read(c + a_off[g] + it[i]);
+#pragma unroll
+                        for (int j = 0; j < kCols; ++j) fb[j] = OB::read(c + b_off[g] + jt[q * kCols + j]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+#pragma unroll
+                            for (int i = 0; i < kFM; ++i)
+#pragma unroll
+                                for (int j = 0; j < kCols; ++j)
+                                    part[i][j][u % kShortChains] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                        fa[i][u], fb[j][u], part[i][j][u % kShortChains], 0, 0, 0);
+                    }
+                    // this slot's share of the previous part's stores (all of
+                    // them by the last slot, whether or not it computed)
+                    if (q > 0) {
+#pragma unroll
+                        for (int t = 0; t < kPer; ++t) {
+                            const int s = (st * 4 + g) * kPer + t;
+                            if (s < kStores) put(q - 1, s);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kCols; ++j) {
+                const int col = n0 + wn + 32 * (q * kCols + j) + l32;
+                const float bj = bias != nullptr ? bias[col] : 0.0f;
+#pragma unroll
+                for (int i = 0; i < kFM; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        float x = part[i][j][0][v];
+#pragma unroll
+                        for (int c = 1; c < kShortChains; ++c) x += part[i][j][c][v];
+                        x += bj;
+                        if (act == 1) x = gelu(x);
+                        done[i][j][v] = x;
+                    }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kStores; ++s) put(kShortParts - 1, s);
+        return;
+    }
+
     v16f acc[kFM][kFN];
 #pragma unroll
     for (int i = 0; i < kFM; ++i)
 #pragma unroll
         for (int j = 0; j < kFN; ++j) acc[i][j] = v16f{0.0f};
 
-    const int stages = K / kBK;
     copy_stage(lds, 0);
     for (int st = 0; st < stages; ++st) {
         // This wave's copies of stage st have landed; after the barrier
