@@ -92,16 +92,42 @@ KERNEL_SOURCES = {
 }
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments and with runs of white space made one
+    space: what the compiler sees, so that editing a comment does not change
+    a kernel's digest.  String and character literals are kept as written."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(kernel: str = "gemm_f32_mfma") -> str:
-    """Hash of the sources of one kernel family; counter summaries are valid
-    only for this digest."""
+    """Hash of the code (comments excluded) of the sources of one kernel
+    family; counter summaries are valid only for this digest."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_fp32_matrix_gemm_amd", "csrc")
     for name in sorted(KERNEL_SOURCES[kernel]):
         p = os.path.join(csrc, name)
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -64,7 +64,7 @@ __device__ __forceinline__ void unroll_for(F &&f)
 }
 
 // BM x BN of C per workgroup, BK bf16 per stage, WAVES_M x WAVES_N waves,
-// NBUF LDS stage buffers (copies in flight: NBUF - 1), GROUP_M tile-rows per
+// NBUF LDS stage buffers (copies issued NBUF - 1 stages ahead), GROUP_M tile-rows per
 // group of the launch order, FOLD stages per accumulation chunk (0: one
 // running accumulator), STAGGER: the second half of the waves issues its
 // share of the next stage's copies after the first MFMA step instead of
@@ -317,6 +317,10 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
                     // NB - 2 later stages are outstanding; after the barrier
                     // every wave's share is visible and every wave is done
                     // with stage st - 1, whose buffer the next copy refills.
+                    // (__syncthreads' release fence makes the compiler wait
+                    // for all outstanding copies before the barrier anyway;
+                    // a fence-less barrier that kept them in flight was
+                    // measured no faster: 4096^3 1198 vs 1204 TFLOP/s.)
                     if (NB == 2 || st + NB - 2 >= full)
                         wait_vm<0>();
                     else

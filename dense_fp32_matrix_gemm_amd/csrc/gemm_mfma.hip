@@ -113,7 +113,7 @@ template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int WPE_, int GRO
           int STAGGER_ = 0>
 struct Config {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
-    static constexpr int nbuf = NBUF_;  // LDS stage buffers (copies in flight: NBUF - 1)
+    static constexpr int nbuf = NBUF_;  // LDS stage buffers (copies issued NBUF - 1 stages ahead)
     static constexpr int fold = FOLD_;  // stages per accumulation chunk on the copy path
     static constexpr bool prefetch = PREFETCH_;  // read k group t + 1 before group t's MFMAs
     static constexpr bool prio = PRIO_;          // raised issue priority while issuing MFMAs
@@ -483,6 +483,13 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                     // later stages are outstanding); after the barrier every
                     // wave's share is visible, and every wave is done with
                     // stage st - 1, whose buffer the next copy refills.
+                    // __syncthreads' release fence also makes the compiler
+                    // wait for every outstanding copy before the barrier, so
+                    // in effect each stage's copies have one stage to land
+                    // whatever NB is.  A barrier without the fence (keeping
+                    // the later stages in flight) was measured and gained
+                    // nothing (4096^3 138.4 vs 138.3 TFLOP/s; the ragged
+                    // ring 83.2 vs 85.3): the copies are not latency bound.
                     if (NB == 2 || st + NB - 2 >= full)
                         wait_vm<0>();
                     else
@@ -632,14 +639,14 @@ using Default = Config<GEMM_MFMA_CONFIG>;
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
 using SmallDeep = Config<GEMM_MFMA_SMALL_DEEP_CONFIG>;
 // 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU (three 48 KB
-// stage buffers, two stages of copies in flight, 192-k accumulation chunks,
+// stage buffers, copies issued two stages ahead, 192-k accumulation chunks,
 // half the waves copying after k group 1: +0.7-0.9 % on 4096^3).
 // A quarter fewer bytes copied into LDS per flop than the 128 x 128 tile:
 // on 4096^3 136 vs 134 TFLOP/s.  Needs enough tiles to fill every CU twice.
 using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // Large tile when both operands are k-contiguous (A untransposed, B
-// transposed): every DMA row segment is a short run along k, and four
-// 16-k stage buffers in flight hide its latency better (the
+// transposed): every DMA row segment is a short run along k, and 16-k
+// stages in four buffers were measured faster (the
 // 8192 x 1024 x 4096 input-gradient product: 125 -> 129 TFLOP/s; with
 // raised MFMA issue priority 131.1 -> 135.1).
 using DefaultKK = Config<GEMM_MFMA_KK_CONFIG>;
