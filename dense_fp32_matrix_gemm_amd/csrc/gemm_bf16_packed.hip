@@ -54,6 +54,15 @@ struct Bool {
     static constexpr bool value = V;
 };
 
+// Interior stages are copied with buffer loads (1) or global loads (0)
+// into LDS.
+#ifndef GEMM_PACKED_BUFFER_DMA
+#define GEMM_PACKED_BUFFER_DMA 1
+#endif
+#ifndef GEMM_PACKED_RUNTIME_BUFFER
+#define GEMM_PACKED_RUNTIME_BUFFER 1
+#endif
+
 template <int N, int I = 0, class F>
 __device__ __forceinline__ void unroll_for(F &&f)
 {
@@ -142,6 +151,30 @@ struct Tile {
                                              16, 0, 0);
     }
 
+    // The same copies as buffer loads: the stage's offset along k is an
+    // SGPR offset (soff) on a raw buffer descriptor of the operand tile's
+    // first row (no stride, no range limit: the host keeps every offset
+    // below 2^32; the data format untyped loads need on this family), so
+    // each lane keeps only its 32-bit offsets, where global loads would keep
+    // a 64-bit address per copy live across the loop.
+    __device__ static __forceinline__ void dma_buffer(char *lds, const char *row0, uint32_t soff,
+                                                      const uint32_t (&off)[dma_per_wave], int wave)
+    {
+        if (GEMM_LDS_POISON) {
+#pragma unroll
+            for (int q = 0; q < dma_per_wave; ++q)
+                poison16(lds + 1024 * (wave * dma_per_wave + q) + 16 * (threadIdx.x % kWave));
+            poison_wait();
+        }
+        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(row0), short(0),
+                                                            int(0xFFFFFFFFu), int(0x00020000));
+#pragma unroll
+        for (int q = 0; q < dma_per_wave; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void *)(lds + 1024 * (wave * dma_per_wave + q)), 16, off[q],
+                soff, 0, 0);
+    }
+
     // Register staging: vector i = threadIdx.x + threads * q of the tile is
     // row i / vpr, k = 8 * (i % vpr) .. +7.  Elements outside rows x cols of
     // the packed operand (rows along m or n, cols along k) read as zero.
@@ -192,6 +225,29 @@ struct Tile {
     {
         return *reinterpret_cast<const v8bf *>(lds + 16 * slot(p, 2 * g + h));
     }
+
+    // A lane reads rows p0 + 32 i (i = 0, 1, ...).  The swizzle depends only
+    // on r mod 16, so rows 32 apart share it: one byte offset per step g
+    // serves every i, and row p0 + 32 i lies a constant 32 * 16 * vpr bytes
+    // further (an immediate offset of the LDS read), which keeps the
+    // per-lane address registers at BK / 16.
+    static constexpr int kSteps = Cfg::BK / 16;
+    static constexpr int kRowBytes = 16 * vpr;
+    struct Lane {
+        uint32_t off[kSteps];
+    };
+    __device__ static __forceinline__ Lane lane_offsets(int p0, int h)
+    {
+        Lane f;
+#pragma unroll
+        for (int g = 0; g < kSteps; ++g) f.off[g] = uint32_t(16 * slot(p0, 2 * g + h));
+        return f;
+    }
+    // fragment(lds, p0 + 32 i, g, h), from the lane's offsets.
+    __device__ static __forceinline__ v8bf fragment(const char *lds, const Lane &f, int i, int g)
+    {
+        return *reinterpret_cast<const v8bf *>(lds + f.off[g] + i * 32 * kRowBytes);
+    }
 };
 
 template <class Cfg, bool VEC>
@@ -218,6 +274,8 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
     const int half = lane / 32, l32 = lane % 32;
     const int stages = ceil_div(K, BK);
     const int full = K / BK;
+    const typename TA::Lane fra = TA::lane_offsets(wm + l32, half);
+    const typename TB::Lane frb = TB::lane_offsets(wn + l32, half);
 
     constexpr bool kChunked = Cfg::fold > 0;
     v16f acc[FM][FN], part[kChunked ? FM : 1][kChunked ? FN : 1];
@@ -239,9 +297,9 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
         v8bf fa[2][FM], fb[2][FN];
         auto read = [&](int g, int s) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa[s][i] = TA::fragment(la, wm + i * kBlk + l32, g, half);
+            for (int i = 0; i < FM; ++i) fa[s][i] = TA::fragment(la, fra, i, g);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) fb[s][j] = TB::fragment(lb, wn + j * kBlk + l32, g, half);
+            for (int j = 0; j < FN; ++j) fb[s][j] = TB::fragment(lb, frb, j, g);
         };
         read(0, 0);
         // Raised issue priority while this wave feeds the matrix core: the
@@ -294,6 +352,9 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
         for (int q = 0; q < TB::dma_per_wave; ++q) ob[q] = TB::dma_offset(ldb, wave, lane, q);
         const char *ga = reinterpret_cast<const char *>(A + int64_t(m0) * lda);
         const char *gb = reinterpret_cast<const char *>(B + int64_t(n0) * ldb);
+#if GEMM_PACKED_BUFFER_DMA
+        const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+#endif
         constexpr int NB = Cfg::nbuf, FOLD = Cfg::fold;
         constexpr int D = TA::dma_per_wave + TB::dma_per_wave;  // copies per wave per stage
         auto bufp = [&](auto idx) -> char * {
@@ -301,13 +362,31 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
             return I == 0 ? buf0 : I == 1 ? buf1 : I == 2 ? buf2 : buf3;
         };
         auto dma = [&](char *lds, int st) {
+#if GEMM_PACKED_BUFFER_DMA
+            TA::dma_buffer(lds, ga, uint32_t(2 * BK * st), oa, wave_s);
+            TB::dma_buffer(lds + TA::bytes, gb, uint32_t(2 * BK * st), ob, wave_s);
+#else
             TA::dma(lds, ga + 2 * BK * st, oa, wave);
             TB::dma(lds + TA::bytes, gb + 2 * BK * st, ob, wave);
+#endif
         };
         dma(buf0, 0);
         if (NB > 2 && 1 < full) dma(bufp(Int<1 % NB>{}), 1);
         if (NB > 3 && 2 < full) dma(bufp(Int<2 % NB>{}), 2);
         constexpr int TRIP = NB > FOLD ? NB : FOLD;
+        if constexpr (GEMM_PACKED_RUNTIME_BUFFER && NB == 2 && FOLD == 0 && !Cfg::stagger) {
+            // One running sum in two buffers: a plain loop that picks the
+            // buffer from the stage's parity, so one set of fragment
+            // addresses is live instead of one per unrolled stage.
+            for (int st = 0; st < full; ++st) {
+                wait_vm<0>();
+                __syncthreads();
+                char *cur = (st & 1) ? buf1 : buf0;
+                char *nxt = (st & 1) ? buf0 : buf1;
+                if (st + 1 < full) dma(nxt, st + 1);
+                compute(cur, Bool<true>{}, Bool<true>{}, [] {});
+            }
+        } else
         for (int s = 0; s < full; s += TRIP) {
             unroll_for<TRIP>([&](auto bi) {
                 constexpr int b = decltype(bi)::value;
@@ -456,9 +535,10 @@ void dispatch(const PackedProblem &p, hipStream_t s)
     const int64_t tiles = int64_t(tiles_m) * tiles_n;
     const bool vec = reinterpret_cast<uintptr_t>(p.A) % 16 == 0 && reinterpret_cast<uintptr_t>(p.B) % 16 == 0 &&
                      p.lda % 8 == 0 && p.ldb % 8 == 0;
-    // The DMA offsets are 32-bit byte offsets from a tile's first row.
-    const int dma_ok = int64_t(Cfg::BM) * p.lda * 2 < (int64_t(1) << 32) &&
-                       int64_t(Cfg::BN) * p.ldb * 2 < (int64_t(1) << 32);
+    // The DMA offsets are 32-bit byte offsets from a tile's first row, to
+    // which the stage's offset along k (less than one row) is added.
+    const int dma_ok = int64_t(Cfg::BM + 1) * p.lda * 2 < (int64_t(1) << 32) &&
+                       int64_t(Cfg::BN + 1) * p.ldb * 2 < (int64_t(1) << 32);
     for (int64_t base = 0; base < tiles; base += kMaxGrid) {
         const int64_t n = tiles - base < kMaxGrid ? tiles - base : kMaxGrid;
         if (vec)
