@@ -245,9 +245,7 @@ struct Tile {
         }
 #pragma unroll
         for (int q = 0; q < dma_per_wave; ++q)
-            if (dma_active(wave, q))
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(origin + off[q]),
-                                                 lds + (wave * dma_per_wave + q) * 256, 16, 0, 0);
+            if (dma_active(wave, q)) copy16_to_lds(lds + (wave * dma_per_wave + q) * 256, origin, off[q]);
     }
 
     // The four k values (one per MFMA u = 0..3) this lane feeds for k group

@@ -176,13 +176,9 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
             poison_wait();
         }
 #pragma unroll
-        for (int q = 0; q < kAPieces; ++q)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(sa + oa[q]),
-                                             dst + (wave * kAPieces + q) * 256, 16, 0, 0);
+        for (int q = 0; q < kAPieces; ++q) copy16_to_lds(dst + (wave * kAPieces + q) * 256, sa, oa[q]);
 #pragma unroll
-        for (int q = 0; q < kBPieces; ++q)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(sb + ob[q]),
-                                             dst + kAFloats + (wave * kBPieces + q) * 256, 16, 0, 0);
+        for (int q = 0; q < kBPieces; ++q) copy16_to_lds(dst + kAFloats + (wave * kBPieces + q) * 256, sb, ob[q]);
     };
 
     // Fragment addresses (floats from a stage's origin) for k group g and

@@ -101,6 +101,27 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// One 16-byte global -> LDS copy per lane: lane l's vector at byte offset
+// off from base (wave-uniform) lands at lds_piece + 16 l bytes.  Issued as a
+// buffer load on a raw descriptor of base (no stride, no range limit: the
+// host keeps every offset below 2^32; the data format untyped loads need on
+// this family), so a lane keeps only its 32-bit offset; GEMM_BUFFER_DMA 0
+// issues global_load_lds with a 64-bit address per lane instead.
+#ifndef GEMM_BUFFER_DMA
+#define GEMM_BUFFER_DMA 1
+#endif
+__device__ __forceinline__ void copy16_to_lds(float *lds_piece, const char *base, uint32_t off)
+{
+    if (GEMM_BUFFER_DMA) {
+        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), short(0), int(0xFFFFFFFFu),
+                                                            int(0x00020000));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_piece, 16, off, 0,
+                                                 0, 0);
+    } else {
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const float *>(base + off), lds_piece, 16, 0, 0);
+    }
+}
+
 // GEMM_LDS_POISON 1 builds the race-detection ablation (the library is built
 // with 0): before a stage buffer is refilled, each lane first writes NaN
 // over exactly the LDS bytes its own copies (or stores) of the refill will
