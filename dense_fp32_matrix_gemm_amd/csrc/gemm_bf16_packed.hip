@@ -353,7 +353,11 @@ packed_kernel(int M, int N, int K, const u16 *__restrict__ A, int64_t lda, const
         const char *ga = reinterpret_cast<const char *>(A + int64_t(m0) * lda);
         const char *gb = reinterpret_cast<const char *>(B + int64_t(n0) * ldb);
 #if GEMM_PACKED_BUFFER_DMA
-        const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+        // the wave index in a scalar register for the copies' LDS address
+        // (M0); the mask states its range, which the compiler needs to see
+        // that a copy does not write the buffer being read
+        static_assert((Cfg::waves & (Cfg::waves - 1)) == 0, "a power-of-two wave count");
+        const int wave_s = __builtin_amdgcn_readfirstlane(wave) & (Cfg::waves - 1);
 #endif
         constexpr int NB = Cfg::nbuf, FOLD = Cfg::fold;
         constexpr int D = TA::dma_per_wave + TB::dma_per_wave;  // copies per wave per stage

@@ -296,7 +296,12 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const int m0 = tm * BM, n0 = tn * BN;
     const bool inside = (m0 + BM <= M) && (n0 + BN <= N);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same, in a scalar register
+    // The same, in a scalar register.  The mask states its range, which the
+    // compiler cannot see through the scalar read: without it, a copy's LDS
+    // destination could be anywhere, and the compiler would wait for every
+    // copy in flight before each LDS read.
+    static_assert((Cfg::waves & (Cfg::waves - 1)) == 0, "a power-of-two wave count");
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave) & (Cfg::waves - 1);
     const int kslice = wave / Cfg::waves_mn, wmn = wave % Cfg::waves_mn;
     const int wm = (wmn / Cfg::waves_n) * Cfg::WM, wn = (wmn % Cfg::waves_n) * Cfg::WN;
     const int half = lane / 32, l32 = lane % 32;
@@ -455,8 +460,8 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             return I == 0 ? buf0 : I == 1 ? buf1 : I == 2 ? buf2 : buf3;
         };
         auto dma = [&](float *lds, int stage) {
-            TA::dma(lds, ga + stage * a_step, oa, wave);
-            TB::dma(lds + TA::floats, gb + stage * b_step, ob, wave);
+            TA::dma(lds, ga + stage * a_step, oa, wave_s);
+            TB::dma(lds + TA::floats, gb + stage * b_step, ob, wave_s);
         };
         dma(buf0, 0);
         if (!GEMM_MFMA_SINGLE_BUFFER && NB > 2 && 1 < full) dma(bufp(Int<1 % NB>{}), 1);

@@ -18,8 +18,8 @@
 //    dimensions that are multiples of 4 floats: every tile is interior and
 //    every stage is one DMA copy.  The host checks all of this
 //    (mfma_wide_fits); other problems go to the kernels of gemm_mfma.hip.
-//  * Staging: each 32-k stage is copied global -> LDS with
-//    global_load_lds_dwordx4 one stage ahead into the other buffer (one
+//  * Staging: each 32-k stage is copied global -> LDS with buffer loads
+//    into LDS (copy16_to_lds) one stage ahead into the other buffer (one
 //    barrier per stage).  The buffer is picked at run time from the stage
 //    parity, so the compiler keeps one set of fragment addresses instead of
 //    one per buffer.
@@ -165,6 +165,11 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
     const char *ga = OA::origin(A, m0, lda);
     const char *gb = OB::origin(B, n0, ldb);
     const int64_t a_step = OA::stage_bytes(lda), b_step = OB::stage_bytes(ldb);
+    // The copies' LDS destination goes to M0, a scalar register: take the
+    // wave index from one too, so it is not re-read from a vector register
+    // for every copy (the mask states its range, which the compiler needs
+    // to see that a copy does not write the buffer being read).
+    const int wave_c = __builtin_amdgcn_readfirstlane(wave) & (kWaves - 1);
     auto copy_stage = [&](float *dst, int st) {
         const char *sa = ga + st * a_step;
         const char *sb = gb + st * b_step;
@@ -176,9 +181,9 @@ wide_kernel(int K, const float *__restrict__ A, int64_t lda, const float *__rest
             poison_wait();
         }
 #pragma unroll
-        for (int q = 0; q < kAPieces; ++q) copy16_to_lds(dst + (wave * kAPieces + q) * 256, sa, oa[q]);
+        for (int q = 0; q < kAPieces; ++q) copy16_to_lds(dst + (wave_c * kAPieces + q) * 256, sa, oa[q]);
 #pragma unroll
-        for (int q = 0; q < kBPieces; ++q) copy16_to_lds(dst + kAFloats + (wave * kBPieces + q) * 256, sb, ob[q]);
+        for (int q = 0; q < kBPieces; ++q) copy16_to_lds(dst + kAFloats + (wave_c * kBPieces + q) * 256, sb, ob[q]);
     };
 
     // Fragment addresses (floats from a stage's origin) for k group g and
