@@ -616,13 +616,13 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_SMALL_DEEP_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4, 0
 #endif
 #ifndef GEMM_MFMA_HUGE_CONFIG
-#define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 8, 1, 1, 1, 3, 6, 1, 0, 1
+#define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 8, 1, 1, 1, 2, 8, 1, 0, 1
 #endif
 #ifndef GEMM_MFMA_KK_CONFIG
 #define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1, 1
 #endif
 #ifndef GEMM_MFMA_ONE_ROUND_CONFIG
-#define GEMM_MFMA_ONE_ROUND_CONFIG 128, 128, 32, 4, 2, 4, 8, 1, 1, 1, 3, 6, 1, 1, 1
+#define GEMM_MFMA_ONE_ROUND_CONFIG 128, 128, 32, 4, 2, 4, 8, 1, 1, 1, 2, 6, 1, 1, 1
 #endif
 #ifndef GEMM_MFMA_NARROW_CONFIG
 #define GEMM_MFMA_NARROW_CONFIG 128, 64, 64, 4, 2, 4, 8, 7, 1, 1, 2, 4, 1, 1
@@ -641,11 +641,15 @@ using Default = Config<GEMM_MFMA_CONFIG>;
 // (85.9 vs 83.5): SmallDeep.
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
 using SmallDeep = Config<GEMM_MFMA_SMALL_DEEP_CONFIG>;
-// 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU (three 48 KB
-// stage buffers, copies issued two stages ahead, 192-k accumulation chunks,
-// half the waves copying after k group 1: +0.7-0.9 % on 4096^3).
-// A quarter fewer bytes copied into LDS per flop than the 128 x 128 tile:
-// on 4096^3 136 vs 134 TFLOP/s.  Needs enough tiles to fill every CU twice.
+// 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU (two 48 KB
+// stage buffers, 256-k accumulation chunks, half the waves copying after k
+// group 1: +0.7-0.9 % on 4096^3).  A quarter fewer bytes copied into LDS per
+// flop than the 128 x 128 tile: on 4096^3 136 vs 134 TFLOP/s.  Needs enough
+// tiles to fill every CU twice.  With the copies as buffer loads, two
+// buffers and 256-k chunks beat three buffers and 192-k chunks (4096^3
+// 145.0 vs 143.8-144.2; the 8192 x 1024 x 4096 input gradient 145.8 vs
+// 144.7; relative Frobenius error at 4096^3 about 3e-7); 384-k chunks gained
+// 0.3 % more at 3.5e-7.
 using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // Large tile when both operands are k-contiguous (A untransposed, B
 // transposed): every DMA row segment is a short run along k, and 16-k
@@ -654,7 +658,8 @@ using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // raised MFMA issue priority 131.1 -> 135.1).
 using DefaultKK = Config<GEMM_MFMA_KK_CONFIG>;
 // 128 x 128 tile for grids of at most one tile per CU, where no second
-// workgroup shares a CU: three stage buffers (96 KB), 192-k accumulation
+// workgroup shares a CU: two stage buffers (three before the copies became
+// buffer loads; two measured 143.6-143.8 against 142.4), 192-k accumulation
 // chunks, raised MFMA issue priority and staggered copies, as on the
 // 256 x 128 tile (the 1024 x 4096 x 8192 weight gradient, 256 tiles:
 // 137.4-137.6 vs 132.7-133.1 TFLOP/s; the priority or the stagger alone
