@@ -690,6 +690,16 @@ def main(argv=None) -> int:
                    {"tflops": flops / (t16 * 1e-3) / 1e12, "ms": t16},
                    "torch.mm f32": {"tflops": flops / (t32 * 1e-3) / 1e12, "ms": t32},
                    "gemm_f32 (FP32 MFMA)": {"tflops": flops / (mine * 1e-3) / 1e12, "ms": mine}}
+        # the vendor product with the same output precision as ours (FP32 C
+        # from bf16 operands), where this PyTorch offers it
+        try:
+            torch.mm(ha, hb, out_dtype=torch.float32)
+            t16f = _timed_warm(lambda: torch.mm(ha, hb, out_dtype=torch.float32), 20)
+            context["torch.mm bf16 operands, FP32 output (out_dtype)"] = {
+                "tflops": flops / (t16f * 1e-3) / 1e12, "ms": t16f,
+                "note": "allocates its output on every call"}
+        except (RuntimeError, TypeError) as e:
+            context["torch.mm bf16 operands, FP32 output (out_dtype)"] = {"unavailable": str(e).split("\n")[0][:160]}
         if packed:
             # the packing kernels (HBM-bound: 4 bytes read, 2 written per
             # element) and the fused one-step entry point on the same inputs
