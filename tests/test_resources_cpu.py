@@ -15,7 +15,9 @@ assembly of the code built here).  Checked:
 * the occupancy and LDS footprint each tile configuration is designed
   around: the 256 x 128 and 256 x 256 FP32 tiles run one workgroup of 8
   waves per CU (2 waves per SIMD), the 128 x 128 tile two workgroups
-  (4 waves per SIMD, at most 64 KB of LDS each), the 64 x 64 tiles four.
+  (4 waves per SIMD, at most 64 KB of LDS each), the 64 x 64 ring four,
+  and the 64 x 64 tile with 128-k stages (grids of about one tile per CU)
+  one workgroup with 128 KB of LDS.
 
 The report's figures are printed, so ``pytest -s`` shows the table.
 """
@@ -189,6 +191,11 @@ def test_fp32_tile_occupancy_and_lds(report):
             # two workgroups per CU: 4 waves per SIMD, 64 KB of LDS each
             assert lds <= 64 * 1024 and occ >= 4 and regs <= 128, k["name"]
             seen.add("128x128")
+        elif (bm, bn) == (64, 64) and cfg[2] == 128:
+            # 128-k stages for grids of about one tile per CU: 128 KB of LDS,
+            # one workgroup (two waves per SIMD) per CU
+            assert lds <= 128 * 1024 and occ >= 2, k["name"]
+            seen.add("64x64")
         elif (bm, bn) == (64, 64):
             assert lds <= 64 * 1024 and occ >= 4, k["name"]
             seen.add("64x64")
