@@ -262,6 +262,88 @@ struct Tile {
     }
 };
 
+// A few rows left over below the last whole row of 64 x 64 tiles (M = 64 q
+// + r, r <= kThinMaxRows) would cost a whole row of tiles that run the full
+// k loop for r valid rows each, and with them a partial extra round of
+// workgroups (2049 x 3071 x 769: 110 us against 94 us without its last
+// row).  Instead, extra workgroups placed first in the grid compute those
+// rows as a matrix-vector style product: each takes 64 columns, its waves
+// split k into contiguous slices and each lane sums its column's products
+// in FP32 over its slice; the slices' sums are then added in wave order
+// through LDS (a fixed order: results do not depend on timing), the fused
+// bias and activation applied, and the rows stored.
+constexpr int kThinMaxRows = 4;
+
+// R rows from m_lo; this workgroup's 64 columns; the wave's slice of k.
+// Every load is unconditional (a column past N reads column N - 1 and its
+// products are dropped), so the compiler can issue a batch of them before
+// the first use: the loop is bound by memory latency, not by arithmetic.
+template <int R, bool A_KC, bool B_KC>
+__device__ __forceinline__ void thin_slice(float (&acc)[kThinMaxRows], int m_lo, int col, int k_lo, int k_hi,
+                                           const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
+                                           int64_t ldb)
+{
+    auto ld_b = [&](int k) { return B_KC ? B[int64_t(col) * ldb + k] : B[int64_t(k) * ldb + col]; };
+    auto ld_a = [&](int i, int k) { return A_KC ? A[int64_t(m_lo + i) * lda + k] : A[int64_t(k) * lda + (m_lo + i)]; };
+    constexpr int U = 16;  // loads in flight per row
+    int k = k_lo;
+    for (; k + U <= k_hi; k += U) {
+        float b[U], a[R][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            b[u] = ld_b(k + u);
+#pragma unroll
+            for (int i = 0; i < R; ++i) a[i][u] = ld_a(i, k + u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < R; ++i) acc[i] = fmaf(a[i][u], b[u], acc[i]);
+    }
+    for (; k < k_hi; ++k) {
+        const float b = ld_b(k);
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i] = fmaf(ld_a(i, k), b, acc[i]);
+    }
+}
+
+template <class Cfg, bool A_KC, bool B_KC>
+__device__ __forceinline__ void thin_rows(int m_lo, int rows, int N, int K, const float *__restrict__ A,
+                                          int64_t lda, const float *__restrict__ B, int64_t ldb,
+                                          float *__restrict__ C, int64_t ldc, const float *__restrict__ bias,
+                                          int act, float *red)
+{
+    static_assert(Cfg::waves * kThinMaxRows * kWave <= (Cfg::BM + Cfg::BN) * Cfg::BK,
+                  "the slice sums fit in one stage buffer");
+    const int wave = int(threadIdx.x) / kWave, lane = int(threadIdx.x) % kWave;
+    const int col = int(blockIdx.x) * kWave + lane;
+    const bool col_ok = col < N;
+    const int per = ceil_div(K, Cfg::waves);
+    const int k_lo = wave * per, k_hi = min(K, k_lo + per);
+    float acc[kThinMaxRows];
+#pragma unroll
+    for (int i = 0; i < kThinMaxRows; ++i) acc[i] = 0.0f;
+    const int c = col_ok ? col : N - 1;
+    switch (rows) {
+    case 1: thin_slice<1, A_KC, B_KC>(acc, m_lo, c, k_lo, k_hi, A, lda, B, ldb); break;
+    case 2: thin_slice<2, A_KC, B_KC>(acc, m_lo, c, k_lo, k_hi, A, lda, B, ldb); break;
+    case 3: thin_slice<3, A_KC, B_KC>(acc, m_lo, c, k_lo, k_hi, A, lda, B, ldb); break;
+    default: thin_slice<kThinMaxRows, A_KC, B_KC>(acc, m_lo, c, k_lo, k_hi, A, lda, B, ldb); break;
+    }
+#pragma unroll
+    for (int i = 0; i < kThinMaxRows; ++i) red[(wave * kThinMaxRows + i) * kWave + lane] = acc[i];
+    __syncthreads();
+    if (wave == 0 && col_ok) {
+        for (int i = 0; i < rows; ++i) {
+            float x = 0.0f;
+            for (int w = 0; w < Cfg::waves; ++w) x += red[(w * kThinMaxRows + i) * kWave + lane];
+            if (bias != nullptr) x += bias[col];
+            if (act == 1) x = gelu(x);
+            C[int64_t(m_lo + i) * ldc + col] = x;
+        }
+    }
+}
+
 template <class Cfg, bool A_KC, bool B_KC, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(Cfg::threads, Cfg::threads),
                           amdgpu_waves_per_eu(Cfg::wpe, Cfg::wpe))) void
@@ -269,7 +351,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
             int tiles_m, int tiles_n, int tile_base, int dma_ok, int64_t stride_a,
             int64_t stride_b, int64_t stride_c, int64_t batch_base,
-            const float *__restrict__ bias, int act, int k_total)
+            const float *__restrict__ bias, int act, int k_total, int thin_blocks, int thin_rows_n)
 {
     // Strided batch: grid y is the product index.
     const int64_t bz = batch_base + blockIdx.y;
@@ -291,8 +373,13 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     __shared__ __attribute__((aligned(1024))) float buf2[Cfg::nbuf > 2 ? kStage : 1];
     __shared__ __attribute__((aligned(1024))) float buf3[Cfg::nbuf > 3 ? kStage : 1];
 
+    // Rows M .. M + thin_rows_n - 1 (below the tiles; single products only).
+    if (int(blockIdx.x) < thin_blocks) {
+        thin_rows<Cfg, A_KC, B_KC>(M, thin_rows_n, N, K, A, lda, B, ldb, C, ldc, bias, act, buf0);
+        return;
+    }
     int tm, tn;
-    tile_of<Cfg::group_m>(tile_base + int(blockIdx.x), tiles_m, tiles_n, tm, tn);
+    tile_of<Cfg::group_m>(tile_base + int(blockIdx.x) - thin_blocks, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const bool inside = (m0 + BM <= M) && (n0 + BN <= N);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -682,7 +769,15 @@ void dispatch(const Problem &p, hipStream_t s)
 {
     using TA = Tile<Cfg, Cfg::BM, A_KC>;
     using TB = Tile<Cfg, Cfg::BN, B_KC>;
-    const int tiles_m = ceil_div(p.M, Cfg::BM), tiles_n = ceil_div(p.N, Cfg::BN);
+    // 64-row tiles with at most kThinMaxRows rows left over: those rows go
+    // to the matrix-vector workgroups at the front of the grid, the tiles
+    // cover the rows above them.
+    const int rest = p.M % Cfg::BM;
+    const bool thin = Cfg::BM == 64 && p.batch == 1 && p.k_total == 0 && p.M > Cfg::BM && rest > 0 &&
+                      rest <= kThinMaxRows;
+    const int m_tiles = thin ? p.M - rest : p.M;
+    const int thin_blocks = thin ? ceil_div(p.N, kWave) : 0;
+    const int tiles_m = ceil_div(m_tiles, Cfg::BM), tiles_n = ceil_div(p.N, Cfg::BN);
     const int64_t tiles = int64_t(tiles_m) * tiles_n;
     const int dma_ok = dma_offsets_fit(TA::rows, p.lda) && dma_offsets_fit(TB::rows, p.ldb);
     // One workgroup per tile (grid x) and product (grid y); grids larger
@@ -692,11 +787,12 @@ void dispatch(const Problem &p, hipStream_t s)
         const int64_t nb = p.batch - b0 < kMaxGridY ? p.batch - b0 : kMaxGridY;
         for (int64_t base = 0; base < tiles; base += kMaxGrid) {
             const int64_t n = tiles - base < kMaxGrid ? tiles - base : kMaxGrid;
+            const int extra = base == 0 ? thin_blocks : 0;  // the first launch carries them
             mfma_kernel<Cfg, A_KC, B_KC, VEC>
-                <<<dim3(unsigned(n), unsigned(nb)), dim3(Cfg::threads), 0, s>>>(
-                    p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,
+                <<<dim3(unsigned(n + extra), unsigned(nb)), dim3(Cfg::threads), 0, s>>>(
+                    m_tiles, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,
                     int(base), dma_ok, p.stride_a, p.stride_b, p.stride_c, b0, p.bias, p.act,
-                    p.k_total);
+                    p.k_total, extra, rest);
         }
     }
 }
