@@ -235,7 +235,7 @@ struct Tile {
     }
     // Copy one stage: `origin` is the stage's stored origin (wave-uniform).
     __device__ static __forceinline__ void dma(float *lds, const char *origin,
-                                               const uint32_t (&off)[dma_per_wave], int wave)
+                                               const uint32_t (&off)[dma_per_wave], int wave, uint32_t avail)
     {
         if (GEMM_LDS_POISON) {
 #pragma unroll
@@ -245,7 +245,7 @@ struct Tile {
         }
 #pragma unroll
         for (int q = 0; q < dma_per_wave; ++q)
-            if (dma_active(wave, q)) copy16_to_lds(lds + (wave * dma_per_wave + q) * 256, origin, off[q]);
+            if (dma_active(wave, q)) copy16_to_lds(lds + (wave * dma_per_wave + q) * 256, origin, off[q], avail);
     }
 
     // The four k values (one per MFMA u = 0..3) this lane feeds for k group
@@ -523,8 +523,25 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         }
     };
 
-    if (VEC && dma_ok && inside && full >= 1) {
-        // Interior tile: full stages copied straight into LDS, NBUF - 1 ahead.
+    // Bytes from a tile's first stage origin to the end of each operand's
+    // storage (its last stored element, rounded up to the 16-byte vector
+    // that holds it: the vectors are aligned, so that never crosses a page).
+    const int64_t a_left = ((4 * (A_KC ? int64_t(M - 1) * lda + K : int64_t(K - 1) * lda + M) + 15) & ~int64_t(15)) -
+                           4 * (int64_t(a_r(0)) * lda + a_c(0));
+    const int64_t b_left = ((4 * (B_KC ? int64_t(N - 1) * ldb + K : int64_t(K - 1) * ldb + N) + 15) & ~int64_t(15)) -
+                           4 * (int64_t(b_r(0)) * ldb + b_c(0));
+    // (Edge tiles by DMA on the small tiles, which serve the ragged
+    // mid-size products; the large tiles keep the register-staged edge path,
+    // their scalar registers being fully used.)
+    constexpr bool kEdgeDma = GEMM_BUFFER_DMA && Cfg::BM * Cfg::BN <= 128 * 64;
+    const bool edge_dma = kEdgeDma && a_left < (int64_t(1) << 32) && b_left < (int64_t(1) << 32);
+    if (VEC && dma_ok && (inside || edge_dma) && full >= 1) {
+        // Full stages copied straight into LDS, NBUF - 1 ahead.  Edge tiles
+        // too: their copies stop at the end of the operand's storage (the
+        // buffer loads' range check, with the bytes left from each stage's
+        // origin), and what they read from a row's padding or past the
+        // matrix's last row or column only reaches outputs outside C, which
+        // are never stored.  Interior tiles copy without a limit.
         uint32_t oa[TA::dma_per_wave], ob[TB::dma_per_wave];
 #pragma unroll
         for (int q = 0; q < TA::dma_per_wave; ++q) oa[q] = TA::dma_offset(lda, wave, lane, q);
@@ -546,9 +563,15 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             constexpr int I = decltype(idx)::value;
             return I == 0 ? buf0 : I == 1 ? buf1 : I == 2 ? buf2 : buf3;
         };
+        // 32-bit byte counts: an edge tile copies by DMA only if both fit
+        // (checked above), and a stage's step is below 2^32 (dma_ok).
+        const uint32_t a_left32 = uint32_t(a_left), b_left32 = uint32_t(b_left);
+        const uint32_t a_step32 = uint32_t(a_step), b_step32 = uint32_t(b_step);
         auto dma = [&](float *lds, int stage) {
-            TA::dma(lds, ga + stage * a_step, oa, wave_s);
-            TB::dma(lds + TA::floats, gb + stage * b_step, ob, wave_s);
+            const uint32_t aa = !kEdgeDma || inside ? 0xFFFFFFFFu : a_left32 - uint32_t(stage) * a_step32;
+            const uint32_t ab = !kEdgeDma || inside ? 0xFFFFFFFFu : b_left32 - uint32_t(stage) * b_step32;
+            TA::dma(lds, ga + stage * a_step, oa, wave_s, aa);
+            TB::dma(lds + TA::floats, gb + stage * b_step, ob, wave_s, ab);
         };
         dma(buf0, 0);
         if (!GEMM_MFMA_SINGLE_BUFFER && NB > 2 && 1 < full) dma(bufp(Int<1 % NB>{}), 1);

@@ -110,10 +110,17 @@ __device__ __forceinline__ void wait_vm()
 #ifndef GEMM_BUFFER_DMA
 #define GEMM_BUFFER_DMA 1
 #endif
-__device__ __forceinline__ void copy16_to_lds(float *lds_piece, const char *base, uint32_t off)
+//
+// `avail` is the number of bytes from base to the end of the operand's
+// storage: the hardware's range check then turns a lane whose vector lies
+// past it into a read of zeros instead of a read past the allocation (edge
+// tiles copy whole stages; the rows or columns outside the matrix only feed
+// outputs that are never stored).
+__device__ __forceinline__ void copy16_to_lds(float *lds_piece, const char *base, uint32_t off,
+                                              uint32_t avail = 0xFFFFFFFFu)
 {
     if (GEMM_BUFFER_DMA) {
-        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), short(0), int(0xFFFFFFFFu),
+        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), short(0), int(avail),
                                                             int(0x00020000));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_piece, 16, off, 0,
                                                  0, 0);
