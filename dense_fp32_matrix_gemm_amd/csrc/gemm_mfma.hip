@@ -390,6 +390,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     static_assert((Cfg::waves & (Cfg::waves - 1)) == 0, "a power-of-two wave count");
     const int wave_s = __builtin_amdgcn_readfirstlane(wave) & (Cfg::waves - 1);
     const int kslice = wave / Cfg::waves_mn, wmn = wave % Cfg::waves_mn;
+    const int kslice_s = wave_s / Cfg::waves_mn;  // the same, scalar
     const int wm = (wmn / Cfg::waves_n) * Cfg::WM, wn = (wmn % Cfg::waves_n) * Cfg::WN;
     const int half = lane / 32, l32 = lane % 32;
     const int stages = ceil_div(K, BK);
@@ -428,9 +429,16 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     // PREFETCH_T: read the next group's fragments ahead (the copy path; the
     // register-staged path, whose loaded stage is live across the MFMAs,
     // reads them just in time to stay within the register budget).
-    auto compute = [&](const float *lds, auto mid, auto fresh_t, auto fold_t, auto prefetch_t) {
+    // TAIL_T: the stage holds the last kv < BK k values of the product and
+    // whatever follows them (zeros on the register-staged path; on the copy
+    // path the next row's values, or zeros past the end of the storage): the
+    // k groups past kv are skipped (a slice's first group still runs, to
+    // start its chunk) and each fragment value past kv is replaced by zero.
+    auto compute = [&](const float *lds, auto mid, auto fresh_t, auto fold_t, auto prefetch_t, auto tail_t,
+                       int kv) {
         constexpr bool kFresh = decltype(fresh_t)::value;
         constexpr bool kFold = decltype(fold_t)::value;
+        constexpr bool kTail = decltype(tail_t)::value;
         constexpr bool kPrefetch = Cfg::prefetch && decltype(prefetch_t)::value && !(Cfg::BM == 256 && !A_KC && B_KC);
         const float *la = lds;
         const float *lb = lds + TA::floats;
@@ -449,12 +457,25 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         if constexpr (Cfg::prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < kGroups; ++t) {
+            const int g = Cfg::ksplit == 1 ? t : t * Cfg::ksplit + kslice_s;
+            if (kTail && t > 0 && 8 * g >= kv) break;
             const int cur = kPrefetch ? (t & 1) : 0;
             if (!kPrefetch)
                 read(t, 0);
             else if (t + 1 < kGroups)
                 read(t + 1, (t + 1) & 1);
             if (Cfg::ksplit == 1 && t == Cfg::write_g) mid();
+            if (kTail) {
+                // lane half h feeds k = 8g + 4h + u
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool ok = 8 * g + 4 * half + u < kv;
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) fa[cur][i][u] = ok ? fa[cur][i][u] : 0.0f;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) fb[cur][j][u] = ok ? fb[cur][j][u] : 0.0f;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -515,9 +536,9 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                 compute(cur, [&] {
                     TA::store(nxt, ra);
                     TB::store(nxt + TA::floats, rb);
-                }, Yes{}, Yes{}, No{});
+                }, Yes{}, Yes{}, No{}, No{}, BK);
             } else {
-                compute(cur, nothing, Yes{}, Yes{}, No{});
+                compute(cur, nothing, Yes{}, Yes{}, No{}, No{}, BK);
             }
             __syncthreads();
         }
@@ -567,15 +588,26 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         // (checked above), and a stage's step is below 2^32 (dma_ok).
         const uint32_t a_left32 = uint32_t(a_left), b_left32 = uint32_t(b_left);
         const uint32_t a_step32 = uint32_t(a_step), b_step32 = uint32_t(b_step);
+        // Where copies can be range-limited, the partial last stage (K % BK
+        // k values) is copied like the full ones, a stage ahead, with the
+        // limit on every tile: its copy reads on past k = K into the storage
+        // that follows (the next row, or zeros past the end), values that
+        // the tail compute replaces by zeros.  (Not when both operands are
+        // stored k-major: that layout has no scalar registers to spare, and
+        // keeps the register-staged tail.)
+        constexpr bool kTailDma = kEdgeDma && !GEMM_MFMA_SINGLE_BUFFER && (A_KC || B_KC);
+        const bool tail_dma = kTailDma && edge_dma && full < stages;
+        const int ndma = full + int(tail_dma);  // stages copied into LDS
         auto dma = [&](float *lds, int stage) {
-            const uint32_t aa = !kEdgeDma || inside ? 0xFFFFFFFFu : a_left32 - uint32_t(stage) * a_step32;
-            const uint32_t ab = !kEdgeDma || inside ? 0xFFFFFFFFu : b_left32 - uint32_t(stage) * b_step32;
+            const bool open = !kEdgeDma || (inside && (!kTailDma || stage < full));
+            const uint32_t aa = open ? 0xFFFFFFFFu : a_left32 - uint32_t(stage) * a_step32;
+            const uint32_t ab = open ? 0xFFFFFFFFu : b_left32 - uint32_t(stage) * b_step32;
             TA::dma(lds, ga + stage * a_step, oa, wave_s, aa);
             TB::dma(lds + TA::floats, gb + stage * b_step, ob, wave_s, ab);
         };
         dma(buf0, 0);
-        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 2 && 1 < full) dma(bufp(Int<1 % NB>{}), 1);
-        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 3 && 2 < full) dma(bufp(Int<2 % NB>{}), 2);
+        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 2 && 1 < ndma) dma(bufp(Int<1 % NB>{}), 1);
+        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 3 && 2 < ndma) dma(bufp(Int<2 % NB>{}), 2);
         // TRIP stages per trip (a multiple of NB and of FOLD) so that each
         // buffer and each chunk boundary is a compile-time choice.
         constexpr int TRIP = NB > FOLD ? NB : FOLD;
@@ -588,7 +620,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                     // buffer -- copy, barrier, compute, barrier, next copy.
                     wait_vm<0>();
                     __syncthreads();
-                    compute(buf0, nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{}, Yes{});
+                    compute(buf0, nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{}, Yes{}, No{}, BK);
                     __syncthreads();
                     if (st + 1 < full) dma(buf0, st + 1);
                 } else if (st < full) {
@@ -603,7 +635,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                     // the later stages in flight) was measured and gained
                     // nothing (4096^3 138.4 vs 138.3 TFLOP/s; the ragged
                     // ring 83.2 vs 85.3): the copies are not latency bound.
-                    if (NB == 2 || st + NB - 2 >= full)
+                    if (NB == 2 || st + NB - 2 >= ndma)
                         wait_vm<0>();
                     else
                         wait_vm<(NB - 2) * D>();
@@ -612,30 +644,42 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                     // that copies later in the stage still has the same
                     // count outstanding at the next wait.
                     const bool late = Cfg::stagger && wave >= Cfg::waves / 2;
-                    if (!late && st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
+                    if (!late && st + NB - 1 < ndma) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
                     compute(bufp(Int<b % NB>{}), [&] {
-                        if (late && st + NB - 1 < full) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
-                    }, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{}, Yes{});
+                        if (late && st + NB - 1 < ndma) dma(bufp(Int<(b + NB - 1) % NB>{}), st + NB - 1);
+                    }, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{}, Yes{}, No{}, BK);
                 }
             });
         }
         if (full % FOLD != 0) fold_part();  // the last chunk was cut short
-        __syncthreads();  // every wave is done with the last full stage's buffer
-        if (full < stages) {
-            // The partial last stage, predicated, through registers.  Its
-            // thread index is derived afresh (the lane counted from the full
-            // execution mask, the wave from a scalar register) and its
-            // fragments are read as in the loop, so that nothing besides the
-            // accumulators has to stay live across the loop for it.
-            const int tid = kWave * wave_s + int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
-            v4f ra[TA::per_thread], rb[TB::per_thread];
-            TA::Load::template load<true, VEC>(opa, a_r(full * BK), a_c(full * BK), ra, tid);
-            TB::Load::template load<true, VEC>(opb, b_r(full * BK), b_c(full * BK), rb, tid);
-            TA::store(buf0, ra, tid);
-            TB::store(buf0 + TA::floats, rb, tid);
+        if (tail_dma) {
+            // The partial stage has landed in buffer full % NB.
+            wait_vm<0>();
             __syncthreads();
-            compute(buf0, nothing, Yes{}, Yes{}, Yes{});
+            const int tb = full % NB;
+            compute(tb == 0 ? buf0 : tb == 1 ? buf1 : tb == 2 ? buf2 : buf3, nothing, Yes{}, Yes{}, Yes{}, Yes{},
+                    K - full * BK);
             __syncthreads();
+        } else {
+            __syncthreads();  // every wave is done with the last full stage's buffer
+            if (full < stages) {
+                // The partial last stage, predicated, through registers.
+                // Its thread index is derived afresh (the lane counted from
+                // the full execution mask, the wave from a scalar register)
+                // and its fragments are read as in the loop, so that nothing
+                // besides the accumulators has to stay live across the loop
+                // for it.
+                const int tid =
+                    kWave * wave_s + int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+                v4f ra[TA::per_thread], rb[TB::per_thread];
+                TA::Load::template load<true, VEC>(opa, a_r(full * BK), a_c(full * BK), ra, tid);
+                TB::Load::template load<true, VEC>(opb, b_r(full * BK), b_c(full * BK), rb, tid);
+                TA::store(buf0, ra, tid);
+                TB::store(buf0 + TA::floats, rb, tid);
+                __syncthreads();
+                compute(buf0, nothing, Yes{}, Yes{}, Yes{}, Yes{}, K - full * BK);
+                __syncthreads();
+            }
         }
     } else {
         v4f ra[TA::per_thread], rb[TB::per_thread];
