@@ -267,17 +267,27 @@ struct Tile {
 // k loop for r valid rows each, and with them a partial extra round of
 // workgroups (2049 x 3071 x 769: 110 us against 94 us without its last
 // row).  Instead, extra workgroups placed first in the grid compute those
-// rows as a matrix-vector style product: each takes 64 columns, its waves
-// split k into contiguous slices and each lane sums its column's products
-// in FP32 over its slice; the slices' sums are then added in wave order
-// through LDS (a fixed order: results do not depend on timing), the fused
-// bias and activation applied, and the rows stored.
+// rows as a matrix-vector style product: each takes kWave / kThinSplit
+// columns; k is cut into waves x kThinSplit contiguous slices, one per
+// wave and lane group, and each lane sums its column's products in FP32
+// over its slice; the slices' sums are then added in slice order through
+// LDS (a fixed order: results do not depend on timing), the fused bias and
+// activation applied, and the rows stored.  The extra workgroups hold tile
+// slots while the tiles start, so they are made short: many of them, each
+// with a few batches of loads per lane.
 constexpr int kThinMaxRows = 4;
+#ifndef GEMM_THIN_SPLIT
+#define GEMM_THIN_SPLIT 4
+#endif
+constexpr int kThinSplit = GEMM_THIN_SPLIT;  // lane groups per wave (k slices per wave)
+constexpr int kThinCols = kWave / kThinSplit;  // columns per workgroup
+static_assert(kWave % kThinSplit == 0, "whole lane groups");
 
-// R rows from m_lo; this workgroup's 64 columns; the wave's slice of k.
-// Every load is unconditional (a column past N reads column N - 1 and its
-// products are dropped), so the compiler can issue a batch of them before
-// the first use: the loop is bound by memory latency, not by arithmetic.
+// R rows from m_lo; this lane's column; its slice [k_lo, k_hi) of k.  Every
+// load is unconditional (a load past the slice reads its last element and
+// the product is dropped), so the compiler issues a whole batch of them
+// before the first use: the loop is bound by memory latency, not by
+// arithmetic.
 template <int R, bool A_KC, bool B_KC>
 __device__ __forceinline__ void thin_slice(float (&acc)[kThinMaxRows], int m_lo, int col, int k_lo, int k_hi,
                                            const float *__restrict__ A, int64_t lda, const float *__restrict__ B,
@@ -286,25 +296,24 @@ __device__ __forceinline__ void thin_slice(float (&acc)[kThinMaxRows], int m_lo,
     auto ld_b = [&](int k) { return B_KC ? B[int64_t(col) * ldb + k] : B[int64_t(k) * ldb + col]; };
     auto ld_a = [&](int i, int k) { return A_KC ? A[int64_t(m_lo + i) * lda + k] : A[int64_t(k) * lda + (m_lo + i)]; };
     constexpr int U = 16;  // loads in flight per row
-    int k = k_lo;
-    for (; k + U <= k_hi; k += U) {
+    auto batch = [&](int k, auto clamp_t) {
+        constexpr bool kClamp = decltype(clamp_t)::value;
         float b[U], a[R][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            b[u] = ld_b(k + u);
+            const int kk = kClamp ? min(k + u, k_hi - 1) : k + u;
+            b[u] = ld_b(kk);
 #pragma unroll
-            for (int i = 0; i < R; ++i) a[i][u] = ld_a(i, k + u);
+            for (int i = 0; i < R; ++i) a[i][u] = ld_a(i, kk);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int i = 0; i < R; ++i) acc[i] = fmaf(a[i][u], b[u], acc[i]);
-    }
-    for (; k < k_hi; ++k) {
-        const float b = ld_b(k);
-#pragma unroll
-        for (int i = 0; i < R; ++i) acc[i] = fmaf(ld_a(i, k), b, acc[i]);
-    }
+            for (int i = 0; i < R; ++i) acc[i] = !kClamp || k + u < k_hi ? fmaf(a[i][u], b[u], acc[i]) : acc[i];
+    };
+    int k = k_lo;
+    for (; k + U <= k_hi; k += U) batch(k, Bool<false>{});
+    if (k < k_hi) batch(k, Bool<true>{});
 }
 
 template <class Cfg, bool A_KC, bool B_KC>
@@ -313,13 +322,17 @@ __device__ __forceinline__ void thin_rows(int m_lo, int rows, int N, int K, cons
                                           float *__restrict__ C, int64_t ldc, const float *__restrict__ bias,
                                           int act, float *red)
 {
-    static_assert(Cfg::waves * kThinMaxRows * kWave <= (Cfg::BM + Cfg::BN) * Cfg::BK,
+    constexpr int kSlices = Cfg::waves * kThinSplit;
+    static_assert(kSlices * kThinMaxRows * kThinCols <= (Cfg::BM + Cfg::BN) * Cfg::BK,
                   "the slice sums fit in one stage buffer");
     const int wave = int(threadIdx.x) / kWave, lane = int(threadIdx.x) % kWave;
-    const int col = int(blockIdx.x) * kWave + lane;
+    const int first = int(blockIdx.x) * kThinCols;
+    if (first >= N) return;  // a workgroup of the rounding to whole XCD rounds
+    const int cl = lane % kThinCols, slice = wave * kThinSplit + lane / kThinCols;
+    const int col = first + cl;
     const bool col_ok = col < N;
-    const int per = ceil_div(K, Cfg::waves);
-    const int k_lo = wave * per, k_hi = min(K, k_lo + per);
+    const int per = ceil_div(K, kSlices);
+    const int k_lo = min(K, slice * per), k_hi = min(K, k_lo + per);
     float acc[kThinMaxRows];
 #pragma unroll
     for (int i = 0; i < kThinMaxRows; ++i) acc[i] = 0.0f;
@@ -331,12 +344,12 @@ __device__ __forceinline__ void thin_rows(int m_lo, int rows, int N, int K, cons
     default: thin_slice<kThinMaxRows, A_KC, B_KC>(acc, m_lo, c, k_lo, k_hi, A, lda, B, ldb); break;
     }
 #pragma unroll
-    for (int i = 0; i < kThinMaxRows; ++i) red[(wave * kThinMaxRows + i) * kWave + lane] = acc[i];
+    for (int i = 0; i < kThinMaxRows; ++i) red[(slice * kThinMaxRows + i) * kThinCols + cl] = acc[i];
     __syncthreads();
-    if (wave == 0 && col_ok) {
+    if (wave == 0 && lane < kThinCols && col_ok) {
         for (int i = 0; i < rows; ++i) {
             float x = 0.0f;
-            for (int w = 0; w < Cfg::waves; ++w) x += red[(w * kThinMaxRows + i) * kWave + lane];
+            for (int q = 0; q < kSlices; ++q) x += red[(q * kThinMaxRows + i) * kThinCols + cl];
             if (bias != nullptr) x += bias[col];
             if (act == 1) x = gelu(x);
             C[int64_t(m_lo + i) * ldc + col] = x;
@@ -843,7 +856,8 @@ void dispatch(const Problem &p, hipStream_t s)
     const bool thin = Cfg::BM == 64 && p.batch == 1 && p.k_total == 0 && p.M > Cfg::BM && rest > 0 &&
                       rest <= kThinMaxRows;
     const int m_tiles = thin ? p.M - rest : p.M;
-    const int thin_blocks = thin ? ceil_div(p.N, kWave) : 0;
+    // (a multiple of the XCD count, so that tile t still runs on XCD t % 8)
+    const int thin_blocks = thin ? kXcds * ceil_div(ceil_div(p.N, kThinCols), kXcds) : 0;
     const int tiles_m = ceil_div(m_tiles, Cfg::BM), tiles_n = ceil_div(p.N, Cfg::BN);
     const int64_t tiles = int64_t(tiles_m) * tiles_n;
     const int dma_ok = dma_offsets_fit(TA::rows, p.lda) && dma_offsets_fit(TB::rows, p.ldb);
