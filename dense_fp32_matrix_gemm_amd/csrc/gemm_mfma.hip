@@ -704,10 +704,92 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         staged(0);
     }
 
-    // Sum the k-slices' partial tiles, pairwise through the (now idle)
-    // stage buffers: at each level the upper half of the slices writes, the
-    // lower half adds.  Every stage buffer holds at least one BM x BN tile.
-    if (Cfg::ksplit > 1) {
+    // Epilogue for accumulator slots V0 .. V1 - 1.  Lane l of a 32 x 32
+    // block holds column l % 32 and, in accumulator slot v, row 8 * (v / 4)
+    // + 4 * (l / 32) + v % 4.  The fused variant adds bias[column] and
+    // applies the activation before the store (both flags are uniform over
+    // the launch).  The lane's position is derived afresh -- the lane index
+    // counted from the (full) execution mask, the wave index from a scalar
+    // register -- so that nothing lane-dependent has to stay in a vector
+    // register across the k loop.
+    auto epilogue = [&](auto v0_t, auto v1_t) {
+        constexpr int V0 = decltype(v0_t)::value, V1 = decltype(v1_t)::value;
+        const int e_lane = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+        const int e_wmn = wave_s % Cfg::waves_mn;
+        const int e_wm = (e_wmn / Cfg::waves_n) * Cfg::WM, e_wn = (e_wmn % Cfg::waves_n) * Cfg::WN;
+        const int e_l32 = e_lane % 32, e_half = e_lane / 32;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + e_wn + j * kBlk + e_l32;
+                const float bj = (bias != nullptr && col < N) ? bias[col] : 0.0f;
+#pragma unroll
+                for (int v = V0; v < V1; ++v) {
+                    const int row = m0 + e_wm + i * kBlk + 8 * (v / 4) + 4 * e_half + (v % 4);
+                    float x = acc[i][j][v] + bj;
+                    if (act == 1) x = gelu(x);
+                    if (inside || (row < M && col < N)) {
+                        // C is written once and not read again here: a
+                        // streaming (non-temporal) store, except for split-k
+                        // partials, which the reduction reads straight back
+                        // (64 products of 512 x 512 x 64: 66.3 vs 64.6
+                        // TFLOP/s; 1024^3 97.4 vs 96.4).
+                        if (k_total > 0)
+                            C[int64_t(row) * ldc + col] = x;
+                        else
+                            __builtin_nontemporal_store(x, &C[int64_t(row) * ldc + col]);
+                    }
+                }
+            }
+    };
+
+    if constexpr (Cfg::ksplit == 2) {
+        // Two k-slices: each finishes half of every block's rows.  Slice 0
+        // keeps accumulator slots 0-7 and hands 8-15 to slice 1 through the
+        // (now idle) first stage buffer, slice 1 the reverse; each adds the
+        // half it receives to its own and stores that half, so all the
+        // waves share the final stores.  a + b equals b + a exactly, so the
+        // sums do not depend on which slice forms them.
+        auto slot = [&](int slice, int i, int j, int vv) {
+            return ((((slice * Cfg::waves_mn + wmn) * FM + i) * FN + j) * 8 + vv) * kWave + lane;
+        };
+        auto give = [&](auto v0_t) {
+            constexpr int V0 = decltype(v0_t)::value;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int vv = 0; vv < 8; ++vv) buf0[slot(kslice, i, j, vv)] = acc[i][j][V0 + vv];
+        };
+        auto take = [&](auto v0_t) {
+            constexpr int V0 = decltype(v0_t)::value;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int vv = 0; vv < 8; ++vv) acc[i][j][V0 + vv] += buf0[slot(1 - kslice, i, j, vv)];
+        };
+        if (kslice_s == 0)
+            give(Int<8>{});
+        else
+            give(Int<0>{});
+        __syncthreads();
+        if (kslice_s == 0) {
+            take(Int<0>{});
+            epilogue(Int<0>{}, Int<8>{});
+        } else {
+            take(Int<8>{});
+            epilogue(Int<8>{}, Int<16>{});
+        }
+        return;
+    } else if constexpr (Cfg::ksplit > 1) {
+        // Sum the k-slices' partial tiles, pairwise through the (now idle)
+        // stage buffers: at each level the upper half of the slices writes,
+        // the lower half adds.  Every stage buffer holds at least one BM x BN
+        // tile.
 #pragma unroll
         for (int width = Cfg::ksplit / 2; width >= 1; width /= 2) {
             const bool writer = kslice >= width && kslice < 2 * width;
@@ -736,41 +818,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         }
         if (kslice != 0) return;  // slice 0 holds the sum; no barrier follows
     }
-
-    // Epilogue.  Lane l of a 32 x 32 block holds column l % 32 and, in
-    // accumulator slot v, row 8 * (v / 4) + 4 * (l / 32) + v % 4.  The fused
-    // variant adds bias[column] and applies the activation before the store
-    // (both flags are uniform over the launch).  The lane's position is
-    // derived afresh -- the lane index counted from the (full) execution
-    // mask, the wave index from a scalar register -- so that nothing
-    // lane-dependent has to stay in a vector register across the k loop.
-    const int e_lane = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
-    const int e_wmn = wave_s % Cfg::waves_mn;
-    const int e_wm = (e_wmn / Cfg::waves_n) * Cfg::WM, e_wn = (e_wmn % Cfg::waves_n) * Cfg::WN;
-    const int e_l32 = e_lane % 32, e_half = e_lane / 32;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + e_wn + j * kBlk + e_l32;
-            const float bj = (bias != nullptr && col < N) ? bias[col] : 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + e_wm + i * kBlk + 8 * (v / 4) + 4 * e_half + (v % 4);
-                float x = acc[i][j][v] + bj;
-                if (act == 1) x = gelu(x);
-                if (inside || (row < M && col < N)) {
-                    // C is written once and not read again here: a streaming
-                    // (non-temporal) store, except for split-k partials, which
-                    // the reduction reads straight back (64 products of
-                    // 512 x 512 x 64: 66.3 vs 64.6 TFLOP/s; 1024^3 97.4 vs 96.4).
-                    if (k_total > 0)
-                        C[int64_t(row) * ldc + col] = x;
-                    else
-                        __builtin_nontemporal_store(x, &C[int64_t(row) * ldc + col]);
-                }
-            }
-        }
+    epilogue(Int<0>{}, Int<16>{});
 }
 
 #ifndef GEMM_MFMA_CONFIG
