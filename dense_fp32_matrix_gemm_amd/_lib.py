@@ -22,7 +22,7 @@ ALGOS = {"auto": ALGO_AUTO, "mfma": ALGO_MFMA, "fma": ALGO_FMA, "tiled": ALGO_TI
 # gemm_f32_plan codes (enum gemm_f32_plan_code)
 PLANS = {0: "nothing", 1: "zero-fill", 2: "mfma-256x256", 3: "mfma-256x128", 4: "mfma-128x128",
          5: "mfma-128x128-one-round", 6: "mfma-128x128-kk", 7: "mfma-128x64", 8: "mfma-64x64",
-         9: "mfma-64x64-ring"}
+         9: "mfma-64x64-pair"}
 
 # Every symbol include/gemm_f32.h declares, with (restype, argtypes).
 _i64, _ptr, _int, _flt = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float

@@ -827,8 +827,8 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #ifndef GEMM_MFMA_SMALL_CONFIG
 #define GEMM_MFMA_SMALL_CONFIG 64, 64, 128, 2, 2, 4, 8, 3, 1, 2, 2, 1, 1, 1
 #endif
-#ifndef GEMM_MFMA_SMALL_DEEP_CONFIG
-#define GEMM_MFMA_SMALL_DEEP_CONFIG 64, 64, 32, 2, 2, 4, 8, 3, 1, 2, 4, 4, 0
+#ifndef GEMM_MFMA_SMALL_PAIR_CONFIG
+#define GEMM_MFMA_SMALL_PAIR_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 2, 2, 1, 1
 #endif
 #ifndef GEMM_MFMA_HUGE_CONFIG
 #define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 8, 1, 1, 1, 2, 8, 1, 0, 1
@@ -852,12 +852,16 @@ using Default = Config<GEMM_MFMA_CONFIG>;
 // the next k group's fragments before the current group's MFMAs: 1024^3
 // 97.6 vs 95.4).  With the copies as buffer loads, 128-k stages (one per
 // accumulation chunk; 128 KB of LDS) are ahead instead: 1024^3 104.7-104.9
-// vs 103.3-103.5 for 64-k stages.  With
-// more tiles per CU (the ragged 2049 x 3071 x 769 product: six) co-resident
-// workgroups hide latency and 32-k stages in a four-buffer ring are faster
-// (85.9 vs 83.5): SmallDeep.
+// vs 103.3-103.5 for 64-k stages.  With more tiles per CU (the ragged
+// 2049 x 3071 x 769 product: six) two workgroups share a CU and hide each
+// other's barriers and start-up: SmallPair, 64-k stages in two buffers (64 KB
+// of LDS each), 128-k accumulation chunks, the next k group's fragments
+// read ahead and raised MFMA issue priority (111.5-112.3 TFLOP/s there,
+// against 106.8-107.2 for 32-k stages in a four-buffer ring; without the
+// read-ahead 110.5-110.9, without the priority 102.3-102.6, with 64-k or
+// 256-k chunks 109.5-109.9 / 111.2-111.5).
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
-using SmallDeep = Config<GEMM_MFMA_SMALL_DEEP_CONFIG>;
+using SmallPair = Config<GEMM_MFMA_SMALL_PAIR_CONFIG>;
 // 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU (two 48 KB
 // stage buffers, 256-k accumulation chunks, half the waves copying after k
 // group 1: +0.7-0.9 % on 4096^3).  A quarter fewer bytes copied into LDS per
@@ -958,9 +962,13 @@ void dispatch_layout(const Problem &p, hipStream_t s)
 // ragged product 81 -> 86; the 1024 x 4096 x 8192 weight gradient, 256
 // large tiles, stays faster on the large tile).  It is also used when more
 // than a quarter of the large tiles' area would fall outside C (e.g. N = 64).
-// Small tiles from which the deeper-ring variant is used (four per CU).
-#ifndef GEMM_MFMA_SMALL_DEEP_FROM
-#define GEMM_MFMA_SMALL_DEEP_FROM 1024
+// The paired variant once there are more small tiles than CUs (then a
+// second workgroup per CU has work; measured with K = 1024: 1536 x 1024,
+// 384 tiles, 88.2 vs 83.3 TFLOP/s; 2048 x 1024 116.8 vs 109.4; 1600 x 1200
+// x 700 97.5 vs 89.0; at 256 tiles, one per CU, the single workgroup with
+// 128-k stages stays ahead).
+#ifndef GEMM_MFMA_SMALL_PAIR_ABOVE
+#define GEMM_MFMA_SMALL_PAIR_ABOVE 256
 #endif
 #ifndef GEMM_MFMA_SMALL_BELOW
 #define GEMM_MFMA_SMALL_BELOW 256
@@ -1008,7 +1016,7 @@ int plan_mfma(const Problem &p, int tile)
     if (narrow) return GEMM_F32_PLAN_MFMA_128X64;
     if (tile == Small::BM) {
         const int64_t small_tiles = int64_t(ceil_div(p.M, Small::BM)) * ceil_div(p.N, Small::BN) * p.batch;
-        return small_tiles >= GEMM_MFMA_SMALL_DEEP_FROM ? GEMM_F32_PLAN_MFMA_64X64_RING : GEMM_F32_PLAN_MFMA_64X64;
+        return small_tiles > GEMM_MFMA_SMALL_PAIR_ABOVE ? GEMM_F32_PLAN_MFMA_64X64_PAIR : GEMM_F32_PLAN_MFMA_64X64;
     }
     if (tile == Huge::BM) return GEMM_F32_PLAN_MFMA_256X128;
     // A is k-contiguous when untransposed; B when transposed.
@@ -1022,7 +1030,7 @@ hipError_t launch_mfma(const Problem &p, hipStream_t s, int tile)
     switch (plan_mfma(p, tile)) {
     case GEMM_F32_PLAN_MFMA_256X256: return launch_mfma_wide(p, s);
     case GEMM_F32_PLAN_MFMA_128X64: dispatch_layout<Narrow>(p, s); break;
-    case GEMM_F32_PLAN_MFMA_64X64_RING: dispatch_layout<SmallDeep>(p, s); break;
+    case GEMM_F32_PLAN_MFMA_64X64_PAIR: dispatch_layout<SmallPair>(p, s); break;
     case GEMM_F32_PLAN_MFMA_64X64: dispatch_layout<Small>(p, s); break;
     case GEMM_F32_PLAN_MFMA_256X128: dispatch_layout<Huge>(p, s); break;
     case GEMM_F32_PLAN_MFMA_128X128_ONE_ROUND: dispatch_layout<OneRound, DefaultKK>(p, s); break;

@@ -98,7 +98,7 @@ enum gemm_f32_plan_code {
     GEMM_F32_PLAN_MFMA_128X128_KK = 6, /* 128 x 128, both operands k-contiguous */
     GEMM_F32_PLAN_MFMA_128X64 = 7,  /* outputs at most 64 columns wide */
     GEMM_F32_PLAN_MFMA_64X64 = 8,   /* small grids: two k-slices of waves */
-    GEMM_F32_PLAN_MFMA_64X64_RING = 9 /* 64 x 64, 32-k stages in a four-buffer ring */
+    GEMM_F32_PLAN_MFMA_64X64_PAIR = 9 /* 64 x 64, larger grids: 64-k stages, two workgroups per CU */
 };
 
 /* C = op(A) . op(B) on the fastest path (GEMM_F32_ALGO_AUTO). */

@@ -402,7 +402,7 @@ def plan(M, N, K, ta=0, tb=0, A=ALIGNED, B=ALIGNED, lda=None, ldb=None, ldc=None
 
 
 WORKLOAD_PLANS = {
-    "S64": "mfma-64x64", "S1k": "mfma-64x64", "R": "mfma-64x64-ring", "S4k": "mfma-256x128",
+    "S64": "mfma-64x64", "S1k": "mfma-64x64", "R": "mfma-64x64-pair", "S4k": "mfma-256x128",
     "T-fwd": "mfma-256x256", "T-dX": "mfma-256x128", "T-dW": "mfma-128x128-one-round",
     "attn-qk": "mfma-256x256", "attn-pv": "mfma-128x64",
 }
@@ -439,8 +439,12 @@ def test_plan_rules_at_their_edges():
     assert plan(2048, 2048, 2048, tb=1) == "mfma-128x128-kk"
     # narrow outputs: N <= 64 and at least 256 tiles of 128 rows
     assert plan(512, 64, 512, sA=512 * 512, sB=512 * 64, batch=64) == "mfma-128x64"
-    assert plan(512, 65, 512, sA=512 * 512, sB=512 * 65, batch=64) == "mfma-64x64-ring"  # 1024 small tiles
-    assert plan(512, 64, 512, sA=512 * 512, sB=512 * 64, batch=63) == "mfma-64x64"
+    assert plan(512, 65, 512, sA=512 * 512, sB=512 * 65, batch=64) == "mfma-64x64-pair"  # 1024 small tiles
+    assert plan(512, 64, 512, sA=512 * 512, sB=512 * 64, batch=63) == "mfma-64x64-pair"  # 504 small tiles
+    # small tiles: one workgroup per CU up to one tile per CU, two sharing a CU beyond
+    assert plan(1024, 1024, 1024) == "mfma-64x64"             # 256 small tiles
+    assert plan(1088, 1024, 1024) == "mfma-64x64-pair"        # 272
+    assert plan(256, 64, 512, sA=256 * 512, sB=512 * 64, batch=64) == "mfma-64x64"  # 256 (batched)
     # degenerate shapes
     assert plan(0, 64, 64) == "nothing" and plan(64, 0, 64) == "nothing"
     assert plan(64, 64, 0) == "zero-fill"
