@@ -825,7 +825,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 4, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_CONFIG
-#define GEMM_MFMA_SMALL_CONFIG 64, 64, 128, 2, 2, 4, 8, 3, 1, 2, 2, 1, 1, 1
+#define GEMM_MFMA_SMALL_CONFIG 64, 64, 128, 2, 2, 4, 8, 3, 1, 2, 2, 2, 1, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_PAIR_CONFIG
 #define GEMM_MFMA_SMALL_PAIR_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 2, 2, 1, 1
@@ -843,16 +843,18 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_NARROW_CONFIG 128, 64, 64, 4, 2, 4, 8, 7, 1, 1, 2, 4, 1, 1
 #endif
 using Default = Config<GEMM_MFMA_CONFIG>;
-// 64 x 64 tile, two k-slices of 4 waves, 128-k stages in two buffers (the
-// stage is the accumulation chunk): a stage long enough to hide one stage of
-// copy latency with a quarter of the barriers of 32-k stages, for grids of up to a few
-// tiles per CU (1024^3, one tile per CU: 96.3 vs 94.2 TFLOP/s; 64 products
+// 64 x 64 tile, two k-slices of 4 waves, 128-k stages in two buffers,
+// 256-k accumulation chunks: a stage long enough to hide one stage of copy
+// latency with a quarter of the barriers of 32-k stages, for grids of up to
+// one tile per CU (1024^3, one tile per CU: 96.3 vs 94.2 TFLOP/s; 64 products
 // of 512 x 64 x 512: 84.9 vs 82.6, and 85.6 vs 83.9 with raised MFMA issue
 // priority; three or four 64-k buffers or 128-k stages were slower; reading
 // the next k group's fragments before the current group's MFMAs: 1024^3
 // 97.6 vs 95.4).  With the copies as buffer loads, 128-k stages (one per
 // accumulation chunk; 128 KB of LDS) are ahead instead: 1024^3 104.7-104.9
-// vs 103.3-103.5 for 64-k stages.  With more tiles per CU (the ragged
+// vs 103.3-103.5 for 64-k stages; 256-k chunks rather than one per stage
+// 105.7-105.9 vs 105.3-105.4 (two partial chains 104.2, four k-slices of
+// 16 waves 100.4, 64-k stages with 256-k chunks 102.9).  With more tiles per CU (the ragged
 // 2049 x 3071 x 769 product: six) two workgroups share a CU and hide each
 // other's barriers and start-up: SmallPair, 64-k stages in two buffers (64 KB
 // of LDS each), 128-k accumulation chunks, the next k group's fragments
