@@ -181,11 +181,15 @@ struct Tile {
     // floats down the rows, which the compiler pairs into two reads.
     static constexpr int reads = KC ? 1 : 2;
 
-    // KC: a fragment read takes 16 bytes from each of 32 consecutive rows.
-    //   (r & 7) ^ ((r >> 3) & 1) makes any 8 consecutive rows hit 8 different
-    //   16-byte bank groups, and any 16 consecutive rows with equal parity of
-    //   r hit 8 different ones, so it is conflict-free whether the LDS serves
-    //   8 or 16 lanes of a 16-byte read per cycle.
+    // KC: a fragment read takes 16 bytes from each of 32 consecutive rows,
+    //   and the LDS serves 16 lanes of a 16-byte read per cycle, which must
+    //   fall in 16 different 16-byte groups of the 256-byte bank line.  Rows
+    //   of 8 vectors (128 bytes) alternate between the line's halves, and
+    //   (r & 7) ^ ((r >> 3) & 1) gives the 8 rows of each parity among any 16
+    //   consecutive rows 8 different groups.  Rows of 16 or more vectors all
+    //   start a bank line, so r & 15 gives 16 consecutive rows 16 different
+    //   groups (measured: 8 groups left two-way conflicts, 2.5e6 stalled
+    //   cycles per launch of the ragged 2049 x 3071 x 769 product).
     // MC: a fragment read takes 4 bytes from 32 consecutive floats of row k
     //   (lanes 0-31) and of row k + 4 (lanes 32-63); flipping bit 3 of the
     //   vector index every 4 rows puts the two halves in opposite 128-byte
@@ -197,6 +201,7 @@ struct Tile {
         if (!GEMM_MFMA_SWIZZLE) return 0;  // the unswizzled ablation build
         if (KC) {
             if (vpr == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+            if (vpr >= 16) return r & 15;
             return ((r & 7) ^ ((r >> 3) & 1)) & (vpr - 1);
         }
         return (((r >> 2) & 1) << 3) & (vpr - 1);
