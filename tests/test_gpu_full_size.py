@@ -49,7 +49,7 @@ def case(oracle, name, dist):
     return _cache[key]
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL + ["S1k", "R"])
 def test_integer_exact_whole_matrix(oracle, name):
     w, A, B, ref = case(oracle, name, "int8")
     assert np.max(np.abs(ref)) < 2 ** 24
