@@ -84,6 +84,29 @@ def test_integer_exact_batched(ta, tb, gap, shared, shape):
 
 
 @pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_integer_exact_batched_paired_small_tiles(ta, tb):
+    """More 64 x 64 tiles than CUs over the batch (4 x 4 x 20 = 320), with
+    16-byte aligned leading dimensions and strides: the two-workgroups-per-CU
+    tile with its copies into LDS, a partial last k stage (K = 70) and the
+    k-slices' halved final exchange.  Exact against the oracle."""
+    M, N, K, batch = 256, 200, 70, 20
+    w = gi.Workload(f"b{M}x{N}x{K}p", M, N, K, 93, 94, "int8", "int8", ta, tb,
+                    lda=(M if ta else K) + 2 + (2 if ta else 0), ldb=(K if tb else N) + (2 if tb else 4),
+                    ldc=N + 4, batch=batch)
+    assert w.lda_ % 4 == 0 and w.ldb_ % 4 == 0 and w.stride_a % 4 == 0 and w.stride_b % 4 == 0
+    import dense_fp32_matrix_gemm_amd as g
+    plan = g.gemm_f32_plan(M, N, K, 1 << 20, w.lda_, 1 << 20, w.ldb_, w.ldc_, ta, tb, w.stride_a,
+                           w.stride_b, batch)
+    assert g.PLANS[plan] == "mfma-64x64-pair", g.PLANS.get(plan, plan)
+    A, B = w.make_a(), w.make_b()
+    got, pad = split_c(w, run_batched(w, A, B, w.make_c()))
+    assert np.all(pad == np.float32(gi.OUTPUT_PAD))
+    ref = reference(w, A, B)
+    for b in range(batch):
+        P.check_exact(got[b], ref[b], f"{w.name}[{b}] t{ta}{tb}")
+
+
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
 @pytest.mark.parametrize("gap", [1, 3])
 def test_integer_exact_batched_aligned_ld_odd_stride(ta, tb, gap):
     """Leading dimensions that are multiples of 4 with strides that are not:

@@ -57,7 +57,11 @@ def check_fused(got, pre, ref, K, what):
     assert np.linalg.norm(err) <= frob_bound, what
 
 
-CASES = [(37, 45, 29), (129, 257, 95), (300, 200, 512), (2300, 4100, 200)]
+# small tiles (with the extra-row workgroups at M = 129), the 64 x 64 tile
+# two workgroups per CU (1100 x 1000: 288 tiles; 1089 rows: plus one extra
+# row), and the 128 x 128 tile
+CASES = [(37, 45, 29), (129, 257, 95), (300, 200, 512), (1100, 1000, 300), (1089, 1000, 301),
+         (2300, 4100, 200)]
 
 
 @pytest.mark.parametrize("shape", CASES, ids=lambda s: "x".join(map(str, s)))
