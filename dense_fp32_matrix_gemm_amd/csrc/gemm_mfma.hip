@@ -15,19 +15,23 @@
 //    k take a 256 x 128 tile (one workgroup per CU), small grids a 64 x 64
 //    tile whose k groups are split over two slices of waves; the
 //    configurations and where each is used are listed below the kernel.
-//  * Staging, interior tiles: each K stage (BK = 32; 16 or 64 in some
+//  * Staging, interior tiles: each K stage (BK = 32; 16, 64 or 128 in some
 //    configurations) is copied from global memory straight into LDS with
-//    global_load_lds_dwordx4 (each wave instruction moves 64 x 16 bytes; no
-//    registers, no LDS write instructions), issued one or more stages ahead
-//    into another LDS buffer, so one barrier per stage suffices (the double
+//    buffer loads into LDS (buffer_load_dwordx4 ... lds on a raw descriptor
+//    of the stage's origin; each wave instruction moves 64 x 16 bytes; no
+//    registers, no LDS write instructions), issued a stage ahead into
+//    another LDS buffer, so one barrier per stage suffices (the double
 //    buffering of the cuda-oxide book's summary; the page's second barrier
 //    is not needed because the buffer being filled is never the one being
 //    read).
-//  * Staging, edge tiles and the last partial stage: 16-byte (or scalar)
-//    loads into registers with every element predicated, zero outside the
-//    matrix (section 3.3's kernel assumes tile multiples), written to LDS
-//    in the same layout.  Stores to C are predicated.  Barriers are outside
-//    every data-dependent branch.
+//  * Staging, edge tiles and the last partial stage: on the small tiles the
+//    copies go on by DMA with the buffer descriptor's range check stopping
+//    them at the end of each operand's storage, and values past K are
+//    replaced by zero in the fragments; elsewhere 16-byte (or scalar) loads
+//    into registers with every element predicated, zero outside the matrix
+//    (section 3.3's kernel assumes tile multiples), written to LDS in the
+//    same layout.  Stores to C are predicated.  Barriers are outside every
+//    data-dependent branch.
 //  * LDS layout: unpadded, with an XOR swizzle of the 16-byte vectors in
 //    each row (the alternative to padding named in section 3.6): a DMA
 //    instruction writes 1 KB contiguously, so padding is not possible, and
@@ -37,7 +41,7 @@
 //    k = 4 + u for the four MFMAs u = 0..3.  Both operands use the same map,
 //    so every pair (a_ik, b_kj) meets exactly once, and a k-contiguous
 //    operand is read with one 16-byte LDS read per lane per 4 MFMAs.
-//  * Accumulation: each run of 128 k values (192 on the 256 x 128 tile) is
+//  * Accumulation: each run of 128-256 k values (per configuration) is
 //    summed into a fresh MFMA accumulator (the first MFMA of the run takes a
 //    zero addend) and then added into the running tile.  The matrix core
 //    adds one product at a time in FP32, so without this the relative error
