@@ -10,8 +10,9 @@
 // choice.  Rounding once pays off on gfx950 because a bf16 stage is short:
 // a 256 x 256 x 32 stage is about a thousand matrix-core cycles, too short
 // for register-staged FP32 loads to hide their latency, while bf16 tiles
-// copied straight into LDS (global_load_lds_dwordx4) move half the bytes
-// with no register or LDS-write instructions.
+// copied straight into LDS (buffer loads into LDS on a scalar descriptor;
+// GEMM_PACKED_BUFFER_DMA 0 builds the global_load_lds form) move half the
+// bytes with no register or LDS-write instructions.
 //
 // Product kernel layout:
 //  * A BM x BN tile of C per workgroup of WAVES_M x WAVES_N waves; each wave
@@ -24,7 +25,8 @@
 //    each row (the DMA writes 1 KB contiguously; the swizzle replaces the
 //    padding that section 3.6 of the course page "3 . La memoire partagee"
 //    uses against bank conflicts).
-//  * Interior tiles copy full stages by DMA, NBUF - 1 stages ahead, one
+//  * Interior tiles copy full stages by DMA, NBUF - 1 stages ahead (in
+//    effect one: the barrier's release fence drains every copy), one
 //    barrier per stage; edge tiles and a partial last stage go through
 //    registers with every element predicated (zero outside the matrix).
 //  * The 256 x 256 and 256 x 128 tiles keep one accumulator: each MFMA adds
