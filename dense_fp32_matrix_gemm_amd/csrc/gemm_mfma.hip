@@ -144,6 +144,10 @@ struct Config {
                   "a k-slice's partial tile fits in one stage buffer for the reduction");
 };
 
+#ifndef GEMM_MFMA_DEEP
+#define GEMM_MFMA_DEEP 1
+#endif
+
 // GEMM_MFMA_SINGLE_BUFFER 1 builds the ablation without double buffering:
 // one stage buffer, each copy issued after the previous stage's compute and
 // awaited before the next (the same results).
@@ -627,12 +631,46 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             TA::dma(lds, ga + stage * a_step, oa, wave_s, aa);
             TB::dma(lds + TA::floats, gb + stage * b_step, ob, wave_s, ab);
         };
+        // The deep ring (below) issues exactly NB - 1 stages up front,
+        // repeating the last one where there are fewer.
+        constexpr bool kDeep = GEMM_MFMA_DEEP && NB > 2 && !GEMM_MFMA_SINGLE_BUFFER && !Cfg::stagger;
         dma(buf0, 0);
-        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 2 && 1 < ndma) dma(bufp(Int<1 % NB>{}), 1);
-        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 3 && 2 < ndma) dma(bufp(Int<2 % NB>{}), 2);
+        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 2 && (kDeep || 1 < ndma)) dma(bufp(Int<1 % NB>{}), min(1, ndma - 1));
+        if (!GEMM_MFMA_SINGLE_BUFFER && NB > 3 && (kDeep || 2 < ndma)) dma(bufp(Int<2 % NB>{}), min(2, ndma - 1));
         // TRIP stages per trip (a multiple of NB and of FOLD) so that each
         // buffer and each chunk boundary is a compile-time choice.
         constexpr int TRIP = NB > FOLD ? NB : FOLD;
+        constexpr int DTRIP = TRIP * (GEMM_MFMA_DEEP > 0 ? GEMM_MFMA_DEEP : 1);
+        if (kDeep) {
+            // Copies NB - 1 stages ahead that stay in flight across the
+            // barriers: each wave waits for its own copies of the stage it
+            // is about to read, and the barrier is not fenced (a fence would
+            // wait for every copy in flight).  Every stage issues one copy
+            // (past the last stage, the last one again, into a buffer that
+            // is not read), so that a count of outstanding copies names a
+            // stage; the trips of DTRIP whole stages have no branches, so
+            // the compiler can tell which buffer each copy writes and does
+            // not wait for copies before the reads.  (The partial last
+            // stage, if copied, lands in buffer full % NB like any other,
+            // and the repeats after it go to the other buffers.)
+            auto stage = [&](auto bi, int st) {
+                constexpr int b = decltype(bi)::value;
+                wait_vm<(NB - 2) * D>();              // stage st has landed
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS reads are done
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                dma(bufp(Int<(b + NB - 1) % NB>{}), min(st + NB - 1, ndma - 1));
+                compute(bufp(Int<b % NB>{}), nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{}, Yes{},
+                        No{}, BK);
+            };
+            int s = 0;
+            for (; s + DTRIP <= full; s += DTRIP) unroll_for<DTRIP>([&](auto bi) { stage(bi, s + decltype(bi)::value); });
+            if (s < full)
+                unroll_for<DTRIP>([&](auto bi) {
+                    if (s + decltype(bi)::value < full) stage(bi, s + decltype(bi)::value);
+                });
+            wait_vm<0>();
+        } else
         for (int s = 0; s < full; s += TRIP) {
             unroll_for<TRIP>([&](auto bi) {
                 constexpr int b = decltype(bi)::value;
@@ -834,7 +872,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 4, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_CONFIG
-#define GEMM_MFMA_SMALL_CONFIG 64, 64, 128, 2, 2, 4, 8, 3, 1, 2, 2, 2, 1, 1
+#define GEMM_MFMA_SMALL_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 4, 4, 1, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_PAIR_CONFIG
 #define GEMM_MFMA_SMALL_PAIR_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 2, 2, 1, 1
