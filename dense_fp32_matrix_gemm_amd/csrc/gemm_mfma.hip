@@ -878,13 +878,13 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_SMALL_PAIR_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 2, 2, 1, 1
 #endif
 #ifndef GEMM_MFMA_HUGE_CONFIG
-#define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 8, 1, 1, 1, 2, 8, 1, 0, 1
+#define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 4, 1, 1, 1, 3, 6, 1, 0, 0
 #endif
 #ifndef GEMM_MFMA_KK_CONFIG
 #define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1, 1
 #endif
 #ifndef GEMM_MFMA_ONE_ROUND_CONFIG
-#define GEMM_MFMA_ONE_ROUND_CONFIG 128, 128, 32, 4, 2, 4, 8, 1, 1, 1, 2, 6, 1, 1, 1
+#define GEMM_MFMA_ONE_ROUND_CONFIG 128, 128, 32, 4, 2, 4, 8, 1, 1, 1, 4, 8, 1, 0, 0
 #endif
 #ifndef GEMM_MFMA_NARROW_CONFIG
 #define GEMM_MFMA_NARROW_CONFIG 128, 64, 64, 4, 2, 4, 8, 7, 1, 1, 2, 4, 1, 1
@@ -911,15 +911,19 @@ using Default = Config<GEMM_MFMA_CONFIG>;
 // 256-k chunks 109.5-109.9 / 111.2-111.5).
 using Small = Config<GEMM_MFMA_SMALL_CONFIG>;
 using SmallPair = Config<GEMM_MFMA_SMALL_PAIR_CONFIG>;
-// 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU (two 48 KB
-// stage buffers, 256-k accumulation chunks, half the waves copying after k
-// group 1: +0.7-0.9 % on 4096^3).  A quarter fewer bytes copied into LDS per
-// flop than the 128 x 128 tile: on 4096^3 136 vs 134 TFLOP/s.  Needs enough
-// tiles to fill every CU twice.  With the copies as buffer loads, two
-// buffers and 256-k chunks beat three buffers and 192-k chunks (4096^3
-// 145.0 vs 143.8-144.2; the 8192 x 1024 x 4096 input gradient 145.8 vs
-// 144.7; relative Frobenius error at 4096^3 about 3e-7); 384-k chunks gained
-// 0.3 % more at 3.5e-7.
+// 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU: three 48 KB
+// stage buffers whose copies stay in flight across the barriers (two stages
+// ahead), 192-k accumulation chunks, tile-groups of 4 rows.  A quarter fewer
+// bytes copied into LDS per flop than the 128 x 128 tile: on 4096^3 136 vs
+// 134 TFLOP/s in the first build.  Needs enough tiles to fill every CU
+// twice.  History at 4096^3 (and the 8192 x 1024 x 4096 input gradient):
+// with fenced barriers, which drain every copy, two buffers and 256-k
+// chunks with half the waves copying after k group 1 were best (145.0 vs
+// 143.8-144.2 for three buffers; 145.8 vs 144.7); with the copies kept in
+// flight, three buffers reach 148.3-148.4 (147.8-147.9) against 144.3-145.5
+// (145.2-146.0), raised MFMA issue priority costing 1-1.5 %, 96-k chunks
+// 1.5 %; 384-k chunks are level.  Relative Frobenius error at 4096^3 about
+// 3e-7.
 using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // Large tile when both operands are k-contiguous (A untransposed, B
 // transposed): every DMA row segment is a short run along k, and 16-k
@@ -928,12 +932,13 @@ using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // raised MFMA issue priority 131.1 -> 135.1).
 using DefaultKK = Config<GEMM_MFMA_KK_CONFIG>;
 // 128 x 128 tile for grids of at most one tile per CU, where no second
-// workgroup shares a CU: two stage buffers (three before the copies became
-// buffer loads; two measured 143.6-143.8 against 142.4), 192-k accumulation
-// chunks, raised MFMA issue priority and staggered copies, as on the
-// 256 x 128 tile (the 1024 x 4096 x 8192 weight gradient, 256 tiles:
-// 137.4-137.6 vs 132.7-133.1 TFLOP/s; the priority or the stagger alone
-// 133.2 / 134.6).
+// workgroup shares a CU: four stage buffers whose copies stay in flight
+// across the barriers (three stages ahead), 256-k accumulation chunks (the
+// 1024 x 4096 x 8192 weight gradient, 256 tiles: 147.5-147.7 TFLOP/s
+// against 143.0-143.3 for two buffers with fenced barriers, raised MFMA
+// issue priority and staggered copies, which had given 137.4-137.6 against
+// 132.7-133.1 in the first build; with the copies in flight the priority
+// costs 1.7 %, and 128-k chunks 1 %).
 using OneRound = Config<GEMM_MFMA_ONE_ROUND_CONFIG>;
 // 128 x 64 tile for outputs at most 64 columns wide (8 waves of 32 x 32,
 // 64-k stages in two buffers, 256-k accumulation chunks): a quarter fewer
