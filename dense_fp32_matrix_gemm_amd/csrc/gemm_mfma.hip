@@ -869,7 +869,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 }
 
 #ifndef GEMM_MFMA_CONFIG
-#define GEMM_MFMA_CONFIG 128, 128, 32, 4, 2, 4, 8, 3, 1, 1, 2, 4, 1
+#define GEMM_MFMA_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1
 #endif
 #ifndef GEMM_MFMA_SMALL_CONFIG
 #define GEMM_MFMA_SMALL_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 4, 4, 1, 1
@@ -889,6 +889,11 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #ifndef GEMM_MFMA_NARROW_CONFIG
 #define GEMM_MFMA_NARROW_CONFIG 128, 64, 64, 4, 2, 4, 8, 7, 1, 1, 2, 4, 1, 1
 #endif
+// 128 x 128 tile, two workgroups per CU: 16-k stages in four buffers (64 KB)
+// whose copies stay in flight across the barriers, 128-k chunks (against 32-k
+// stages in two buffers: 4096 x 2048 x 1024 138.2-139.0 vs 137.3-137.7
+// TFLOP/s, 3072^2 x 1024 107.5 vs 105.0-105.2, 2560^2 x 2048 114.3-114.4 vs
+// 113.1; raised issue priority lost 1 %).
 using Default = Config<GEMM_MFMA_CONFIG>;
 // 64 x 64 tile, two k-slices of 4 waves, 128-k stages in two buffers,
 // 256-k accumulation chunks: a stage long enough to hide one stage of copy

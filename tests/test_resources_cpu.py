@@ -191,6 +191,10 @@ def test_fp32_tile_occupancy_and_lds(report):
             # two workgroups per CU: 4 waves per SIMD, 64 KB of LDS each
             assert lds <= 64 * 1024 and occ >= 4 and regs <= 128, k["name"]
             seen.add("128x128")
+        elif (bm, bn) == (128, 128) and cfg[2] == 16:
+            # 16-k stages in four buffers: 64 KB, two workgroups per CU
+            assert lds <= 64 * 1024 and occ >= 4 and regs <= 128, k["name"]
+            seen.add("128x128")
         elif (bm, bn) == (128, 128) and cfg[2] == 32 and nbuf == 4:
             # one tile per CU: four 32 KB stage buffers, one workgroup
             assert lds <= 128 * 1024 and occ >= 2, k["name"]
