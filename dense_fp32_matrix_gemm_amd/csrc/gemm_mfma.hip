@@ -111,10 +111,12 @@ constexpr int kBlk = 32;  // MFMA output block edge
 // STAGGER (copy path): the second half of the waves issues its share of the
 // next stage's copies after the fragment reads of k group WRITE_G instead of
 // right after the barrier, so the two waves of a SIMD do not both stall on
-// copy issue at the same time.
+// copy issue at the same time.  CROSS (rings of three or more buffers with
+// prefetch): each barrier also certifies the stage after the one it starts,
+// and a stage reads the next stage's first fragments before its last MFMAs.
 template <int BM_, int BN_, int BK_, int WAVES_M, int WAVES_N, int WPE_, int GROUP_M_,
           int WRITE_G_, int CHAINS_, int KSPLIT_, int NBUF_, int FOLD_, int PREFETCH_, int PRIO_ = 0,
-          int STAGGER_ = 0>
+          int STAGGER_ = 0, int CROSS_ = 0>
 struct Config {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int nbuf = NBUF_;  // LDS stage buffers (copies issued NBUF - 1 stages ahead)
@@ -122,6 +124,7 @@ struct Config {
     static constexpr bool prefetch = PREFETCH_;  // read k group t + 1 before group t's MFMAs
     static constexpr bool prio = PRIO_;          // raised issue priority while issuing MFMAs
     static constexpr bool stagger = STAGGER_;    // half the waves copy after k group WRITE_G
+    static constexpr bool cross = CROSS_;        // read the next stage's first group ahead
     static constexpr int ksplit = KSPLIT_;                 // k-slices of waves
     static constexpr int waves_mn = WAVES_M * WAVES_N;     // waves per k-slice
     static constexpr int waves = waves_mn * KSPLIT_;
@@ -460,26 +463,42 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
     // path the next row's values, or zeros past the end of the storage): the
     // k groups past kv are skipped (a slice's first group still runs, to
     // start its chunk) and each fragment value past kv is replaced by zero.
-    auto compute = [&](const float *lds, auto mid, auto fresh_t, auto fold_t, auto prefetch_t, auto tail_t,
-                       int kv) {
+    constexpr int kGroups = BK / 8 / Cfg::ksplit;  // k groups per slice per stage
+    constexpr bool kPrefetchCfg = Cfg::prefetch && !(Cfg::BM == 256 && !A_KC && B_KC);
+    // The first k group's fragments of the next stage, read ahead by the
+    // previous stage (cross-stage prefetch only).
+    v4f xa[FM], xb[FN];
+    auto read_at = [&](const float *lds, int t, v4f (&ra)[FM], v4f (&rb)[FN]) {
+        const int g = Cfg::ksplit == 1 ? t : t * Cfg::ksplit + kslice;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) ra[i] = TA::fragment(lds, wm + i * kBlk + l32, g, half);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) rb[j] = TB::fragment(lds + TA::floats, wn + j * kBlk + l32, g, half);
+    };
+    // CROSS_T (the copy ring, with prefetch): the first group's fragments
+    // were read ahead (xa, xb), and the last group's MFMAs are preceded by
+    // the read of `next`'s first group, so that after the next barrier a
+    // wave starts its MFMAs without waiting on LDS.
+    auto compute_x = [&](const float *lds, const float *next, auto mid, auto fresh_t, auto fold_t, auto prefetch_t,
+                         auto tail_t, auto cross_t, int kv) {
         constexpr bool kFresh = decltype(fresh_t)::value;
         constexpr bool kFold = decltype(fold_t)::value;
         constexpr bool kTail = decltype(tail_t)::value;
-        constexpr bool kPrefetch = Cfg::prefetch && decltype(prefetch_t)::value && !(Cfg::BM == 256 && !A_KC && B_KC);
-        const float *la = lds;
-        const float *lb = lds + TA::floats;
-        constexpr int kGroups = BK / 8 / Cfg::ksplit;  // k groups per slice per stage
+        constexpr bool kPrefetch = kPrefetchCfg && decltype(prefetch_t)::value;
+        constexpr bool kCross = kPrefetch && decltype(cross_t)::value;
+        static_assert(!kCross || !kTail, "a full stage");
         // With prefetch, the fragments of k group t + 1 are read before the
         // MFMAs of group t, so LDS latency overlaps matrix-core work.
         v4f fa[2][FM], fb[2][FN];
-        auto read = [&](int t, int slot) {
-            const int g = Cfg::ksplit == 1 ? t : t * Cfg::ksplit + kslice;
+        auto read = [&](int t, int slot) { read_at(lds, t, fa[slot], fb[slot]); };
+        if (kCross) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa[slot][i] = TA::fragment(la, wm + i * kBlk + l32, g, half);
+            for (int i = 0; i < FM; ++i) fa[0][i] = xa[i];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) fb[slot][j] = TB::fragment(lb, wn + j * kBlk + l32, g, half);
-        };
-        if (kPrefetch) read(0, 0);
+            for (int j = 0; j < FN; ++j) fb[0][j] = xb[j];
+        } else if (kPrefetch) {
+            read(0, 0);
+        }
         if constexpr (Cfg::prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < kGroups; ++t) {
@@ -490,6 +509,8 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                 read(t, 0);
             else if (t + 1 < kGroups)
                 read(t + 1, (t + 1) & 1);
+            else if (kCross)
+                read_at(next, 0, xa, xb);
             if (Cfg::ksplit == 1 && t == Cfg::write_g) mid();
             if (kTail) {
                 // lane half h feeds k = 8g + 4h + u
@@ -517,7 +538,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             // With prefetch, ask the scheduler to spread the next group's LDS
             // reads between this group's MFMAs (one read, then an even share
             // of the MFMAs) instead of clustering them: +0.5-1.5 %.
-            if (kPrefetch && t + 1 < kGroups) {
+            if (kPrefetch && (t + 1 < kGroups || kCross)) {
                 constexpr int kReads = TA::reads * FM + TB::reads * FN;
                 constexpr int kMfma = 4 * FM * FN;
                 constexpr int per = kMfma / kReads > 0 ? kMfma / kReads : 1;
@@ -532,6 +553,9 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         if constexpr (Cfg::prio) __builtin_amdgcn_s_setprio(0);
         if (Cfg::ksplit > 1 || Cfg::write_g >= kGroups) mid();
         if (kFold) fold_part();
+    };
+    auto compute = [&](const float *lds, auto mid, auto fresh_t, auto fold_t, auto prefetch_t, auto tail_t, int kv) {
+        compute_x(lds, lds, mid, fresh_t, fold_t, prefetch_t, tail_t, No{}, kv);
     };
     auto nothing = [] {};
 
@@ -634,6 +658,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
         // The deep ring (below) issues exactly NB - 1 stages up front,
         // repeating the last one where there are fewer.
         constexpr bool kDeep = GEMM_MFMA_DEEP && NB > 2 && !GEMM_MFMA_SINGLE_BUFFER && !Cfg::stagger;
+        constexpr bool kCross = kDeep && Cfg::cross && kPrefetchCfg;
         dma(buf0, 0);
         if (!GEMM_MFMA_SINGLE_BUFFER && NB > 2 && (kDeep || 1 < ndma)) dma(bufp(Int<1 % NB>{}), min(1, ndma - 1));
         if (!GEMM_MFMA_SINGLE_BUFFER && NB > 3 && (kDeep || 2 < ndma)) dma(bufp(Int<2 % NB>{}), min(2, ndma - 1));
@@ -653,15 +678,28 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
             // not wait for copies before the reads.  (The partial last
             // stage, if copied, lands in buffer full % NB like any other,
             // and the repeats after it go to the other buffers.)
+            //
+            // With kCross, each barrier also certifies the stage after the
+            // one it starts (each wave first waits for its own copies of
+            // both), so a stage reads the next stage's first fragments before
+            // its last MFMAs: the copies then have NB - 2 stages to land
+            // instead of NB - 1.
+            if constexpr (kCross) {
+                wait_vm<(NB - 3) * D>();  // stages 0 and 1 have landed
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                read_at(buf0, 0, xa, xb);
+            }
             auto stage = [&](auto bi, int st) {
                 constexpr int b = decltype(bi)::value;
-                wait_vm<(NB - 2) * D>();              // stage st has landed
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS reads are done
+                wait_vm<(kCross ? NB - 3 : NB > 2 ? NB - 2 : 0) * D>();  // stage st (and st + 1) have landed
+                __builtin_amdgcn_s_waitcnt(0xC07F);    // this wave's LDS reads are done
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
                 dma(bufp(Int<(b + NB - 1) % NB>{}), min(st + NB - 1, ndma - 1));
-                compute(bufp(Int<b % NB>{}), nothing, Bool<b % FOLD == 0>{}, Bool<b % FOLD == FOLD - 1>{}, Yes{},
-                        No{}, BK);
+                compute_x(bufp(Int<b % NB>{}), bufp(Int<(b + 1) % NB>{}), nothing, Bool<b % FOLD == 0>{},
+                          Bool<b % FOLD == FOLD - 1>{}, Yes{}, No{}, Bool<kCross>{}, BK);
             };
             int s = 0;
             for (; s + DTRIP <= full; s += DTRIP) unroll_for<DTRIP>([&](auto bi) { stage(bi, s + decltype(bi)::value); });
@@ -884,7 +922,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1, 1
 #endif
 #ifndef GEMM_MFMA_ONE_ROUND_CONFIG
-#define GEMM_MFMA_ONE_ROUND_CONFIG 128, 128, 32, 4, 2, 4, 8, 1, 1, 1, 4, 8, 1, 0, 0
+#define GEMM_MFMA_ONE_ROUND_CONFIG 128, 128, 32, 4, 2, 4, 8, 1, 1, 1, 4, 8, 1, 0, 0, 1
 #endif
 #ifndef GEMM_MFMA_NARROW_CONFIG
 #define GEMM_MFMA_NARROW_CONFIG 128, 64, 64, 4, 2, 4, 8, 7, 1, 1, 2, 4, 1, 1
@@ -895,10 +933,15 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 // TFLOP/s, 3072^2 x 1024 107.5 vs 105.0-105.2, 2560^2 x 2048 114.3-114.4 vs
 // 113.1; raised issue priority lost 1 %).
 using Default = Config<GEMM_MFMA_CONFIG>;
-// 64 x 64 tile, two k-slices of 4 waves, 128-k stages in two buffers,
-// 256-k accumulation chunks: a stage long enough to hide one stage of copy
-// latency with a quarter of the barriers of 32-k stages, for grids of up to
-// one tile per CU (1024^3, one tile per CU: 96.3 vs 94.2 TFLOP/s; 64 products
+// 64 x 64 tile, two k-slices of 4 waves, for grids of up to one tile per CU:
+// 64-k stages in four buffers (128 KB) whose copies stay in flight across
+// the barriers, 256-k accumulation chunks (1024^3: 108.0-108.9 TFLOP/s
+// against 105.7-106.3 for 128-k stages in two fenced buffers; 32-k stages
+// 102.4, three buffers 105.6, 512-k chunks 107.0, without the read-ahead
+// 104.7, without raised priority 97.7, four k-slices 99.2).  Earlier, with
+// fenced barriers, 128-k stages in two buffers: a stage long enough to hide
+// one stage of copy latency with a quarter of the barriers of 32-k stages
+// (1024^3, one tile per CU: 96.3 vs 94.2 TFLOP/s; 64 products
 // of 512 x 64 x 512: 84.9 vs 82.6, and 85.6 vs 83.9 with raised MFMA issue
 // priority; three or four 64-k buffers or 128-k stages were slower; reading
 // the next k group's fragments before the current group's MFMAs: 1024^3
@@ -943,7 +986,12 @@ using DefaultKK = Config<GEMM_MFMA_KK_CONFIG>;
 // against 143.0-143.3 for two buffers with fenced barriers, raised MFMA
 // issue priority and staggered copies, which had given 137.4-137.6 against
 // 132.7-133.1 in the first build; with the copies in flight the priority
-// costs 1.7 %, and 128-k chunks 1 %).
+// costs 1.7 %, and 128-k chunks 1 %).  Each barrier also certifies the
+// stage after the one it starts, and a stage reads the next stage's first
+// fragments before its last MFMAs (copies two stages ahead instead of
+// three): 148.2-148.8 against 146.7 in one session.  (The same on the
+// 256 x 128 tile, whose copies would then have one stage to land, and on
+// the one-tile-per-CU 64 x 64 tile was level or slower.)
 using OneRound = Config<GEMM_MFMA_ONE_ROUND_CONFIG>;
 // 128 x 64 tile for outputs at most 64 columns wide (8 waves of 32 x 32,
 // 64-k stages in two buffers, 256-k accumulation chunks): a quarter fewer
