@@ -919,7 +919,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_HUGE_CONFIG 256, 128, 32, 4, 2, 2, 4, 1, 1, 1, 3, 6, 1, 0, 0
 #endif
 #ifndef GEMM_MFMA_KK_CONFIG
-#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1, 1
+#define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1, 1, 0, 1
 #endif
 #ifndef GEMM_MFMA_ONE_ROUND_CONFIG
 #define GEMM_MFMA_ONE_ROUND_CONFIG 128, 128, 32, 4, 2, 4, 8, 1, 1, 1, 4, 8, 1, 0, 0, 1
@@ -977,7 +977,13 @@ using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // transposed): every DMA row segment is a short run along k, and 16-k
 // stages in four buffers were measured faster (the
 // 8192 x 1024 x 4096 input-gradient product: 125 -> 129 TFLOP/s; with
-// raised MFMA issue priority 131.1 -> 135.1).
+// raised MFMA issue priority 131.1 -> 135.1).  With the copies kept in
+// flight across the barriers (2048^3 128.7 -> 136.0), and with each barrier
+// also certifying the next stage, whose first fragments are read before the
+// current stage's last MFMAs: 2048^3 136.3-136.8 -> 139.9-140.6, 4096 x 2048
+// x 1024 138.9-139.2 -> 140.4-141.4, 2560^2 x 2048 113.4-113.7 -> 114.9-115.4
+// (one session).  (The other layouts of the 128 x 128 tile would spill
+// registers with this read-ahead at two workgroups per CU.)
 using DefaultKK = Config<GEMM_MFMA_KK_CONFIG>;
 // 128 x 128 tile for grids of at most one tile per CU, where no second
 // workgroup shares a CU: four stage buffers whose copies stay in flight
