@@ -46,7 +46,7 @@ ABLATIONS = {
     "singlebuffer": ["-DGEMM_MFMA_SINGLE_BUFFER=1"],  # MFMA kernel: copy/barrier/compute/barrier
     # MFMA kernel, 256 x 128 tile, one running accumulator instead of chunked
     # sums (misses the 1e-6 error bound: what the chunking costs)
-    "nochunk": ["-DGEMM_MFMA_HUGE_CONFIG=256,128,32,4,2,2,4,1,1,1,3,0,1,0,0"],
+    "nochunk": ["-DGEMM_MFMA_HUGE_CONFIG=256,128,16,4,2,2,4,1,1,1,4,0,1,0,0,1"],
     # race detection: every stage buffer holds NaN between its release and
     # its refill (FP32 MFMA, 256 x 256 and packed bf16 kernels; same results)
     "poison": ["-DGEMM_LDS_POISON=1"],

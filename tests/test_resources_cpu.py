@@ -184,7 +184,7 @@ def test_fp32_tile_occupancy_and_lds(report):
         assert occ >= min(wpe, 2), k["name"]
         stagger = len(cfg) > 14 and cfg[14] == 1
         if (bm, bn) == (256, 128):
-            # at most three 48 KB stage buffers: one workgroup per CU
+            # at most 144 KB of stage buffers (four of 24 KB): one workgroup per CU
             assert lds <= 3 * 48 * 1024 and occ == 2 and regs <= 256, k["name"]
             seen.add("256x128")
         elif (bm, bn) == (128, 128) and nbuf == 2 and not stagger:
