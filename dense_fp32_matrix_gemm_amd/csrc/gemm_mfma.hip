@@ -916,7 +916,7 @@ mfma_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
 #define GEMM_MFMA_SMALL_PAIR_CONFIG 64, 64, 64, 2, 2, 4, 8, 3, 1, 2, 2, 2, 1, 1
 #endif
 #ifndef GEMM_MFMA_HUGE_CONFIG
-#define GEMM_MFMA_HUGE_CONFIG 256, 128, 16, 4, 2, 2, 4, 1, 1, 1, 4, 12, 1, 0, 0, 1
+#define GEMM_MFMA_HUGE_CONFIG 256, 128, 16, 4, 2, 2, 4, 1, 1, 1, 4, 16, 1, 0, 0, 1
 #endif
 #ifndef GEMM_MFMA_KK_CONFIG
 #define GEMM_MFMA_KK_CONFIG 128, 128, 16, 4, 2, 4, 8, 3, 1, 1, 4, 8, 1, 1, 0, 1
@@ -962,7 +962,7 @@ using SmallPair = Config<GEMM_MFMA_SMALL_PAIR_CONFIG>;
 // 256 x 128 tile, 8 waves of 64 x 64, one workgroup per CU: 16-k stages in
 // four 24 KB buffers whose copies stay in flight across the barriers, each
 // barrier also certifying the next stage, whose first fragments are read
-// before the current stage's last MFMAs; 192-k accumulation chunks,
+// before the current stage's last MFMAs; 256-k accumulation chunks,
 // tile-groups of 4 rows.  A quarter fewer
 // bytes copied into LDS per flop than the 128 x 128 tile: on 4096^3 136 vs
 // 134 TFLOP/s in the first build.  Needs enough tiles to fill every CU
@@ -974,8 +974,10 @@ using SmallPair = Config<GEMM_MFMA_SMALL_PAIR_CONFIG>;
 // (145.2-146.0), raised MFMA issue priority costing 1-1.5 %, 96-k chunks
 // 1.5 %; 384-k chunks are level.  16-k stages in four buffers with the
 // read-ahead across the barriers then gave 148.5-149.4 against 148.2-148.4
-// (148.2-148.7 against 147.7-147.8), and without the read-ahead were level.
-// Relative Frobenius error at 4096^3 about 3e-7.
+// (148.2-148.7 against 147.7-147.8), and without the read-ahead were level;
+// 256-k chunks rather than 192-k then gave 150.2-150.3 against 149.4-149.8
+// (149.4-149.7 against 148.9-149.2) on a faster machine.  Relative Frobenius
+// error at 4096^3 about 3e-7.
 using Huge = Config<GEMM_MFMA_HUGE_CONFIG>;
 // Large tile when both operands are k-contiguous (A untransposed, B
 // transposed): every DMA row segment is a short run along k, and 16-k
